@@ -1,0 +1,180 @@
+"""Throughput of the FA2-order attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ai2048]
+
+One step is one fa_fwd call over one batch of the workload (inputs already in
+HBM). Prints ONE JSON line with TFLOPS = 4*B*H*N^2*d / time (halved for causal),
+the roofline position of the kernel, and the float64 CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FA fwd TFLOPS (4·B·H·N²·d, causal halved) and % of bf16 MFMA peak, 1 GPU"
+PEAK_TFLOPS = 2500.0        # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+KERNEL_SOURCES = ("io_aware_exact_fa2_amd/csrc/fa_fwd_kernel.hpp",
+                  "io_aware_exact_fa2_amd/csrc/fa_fwd.hip")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_hbm_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_gpu(w, steps, warmup):
+    import torch
+    import io_aware_exact_fa2_amd as fa
+    import workloads
+
+    q, k, v = (t.to("cuda:0") for t in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_fp16
+    args = (q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream)
+    for _ in range(warmup):
+        st = fn(*args)
+        if st != fa.FA_OK:
+            raise fa.FAError(st)
+    torch.cuda.synchronize()
+    # events on the stream the kernel is launched on
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn(*args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    return ms, wall
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle on whole heads of the same workload until ~budget_s."""
+    import numpy as np
+    import oracle
+    from oracle.attention import default_workers
+    import workloads
+
+    q, k, v = workloads.make_inputs(w)
+    qf, kf, vf = (workloads.to_f64(t) for t in (q, k, v))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    workers = default_workers()
+    done = 0
+    t0 = time.perf_counter()
+    step = max(1, min(len(heads), workers))
+    while done < len(heads):
+        batch = heads[done:done + step]
+        oracle.attention_rows(qf, kf, vf, w.scale, w.causal, batch, np.arange(w.N),
+                              workers=workers)
+        done += len(batch)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() * done / len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": workers, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (b,h) heads of {w.name}, all {w.N} rows each, "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ai2048")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 disables)")
+    ap.add_argument("--also", default="causal8k,long32k,stress4000",
+                    help="extra workloads timed for the 'workloads' field ('' for none)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the attention forward "
+              "here is built and timed on a single MI355X; see DESIGN.md for how it would "
+              "shard.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = workloads.get(a.workload)
+    ms, wall = time_gpu(w, a.steps, a.warmup)
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": traffic}
+    extra = {}
+    for name in [s for s in a.also.split(",") if s]:
+        wx = workloads.get(name)
+        msx, _ = time_gpu(wx, max(5, a.steps // 5), 3)
+        tx = wx.flops() / (msx * 1e-3) / 1e12
+        extra[name] = {"ms": round(msx, 4), "tflops": round(tx, 1),
+                       "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1), "dtype": wx.dtype,
+                       "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d]}
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q, K, V rounded to bf16",
+        "config": {"workload": f"{w.name}: non-causal attention forward" if not w.causal
+                   else f"{w.name}: causal attention forward",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale},
+        "pct_bf16_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "algorithmic_GBps": round(w.min_bytes() / (ms * 1e-3) / 1e9, 1),
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_sha256_16": kernel_hash(),
+        "roofline": roof,
+        "workloads": extra,
+    }
+    if a.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

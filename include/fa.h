@@ -1,0 +1,121 @@
+/*
+ * fa.h — C ABI of the FA2-order attention forward pass for AMD MI355X (gfx950).
+ *
+ * Sources for the operation (web pages on FlashAttention):
+ *  [P1] currybab.bearblog.dev, "Triton으로 FlashAttention 구현하기 전에 -
+ *       FA1, 2 forward pass"
+ *  [P2] iq-universe.github.io, "FlashAttention은 어떻게 O(N²) 메모리 벽을 넘었나"
+ *  [P3] ariser.io, "FlashAttention: 어텐션을 빠르게 만든 건 계산량보다 데이터
+ *       이동이었다"
+ *
+ * The library is stateless: it never allocates device memory, keeps no pointer
+ * after a call returns and needs no workspace (the O(N) extra memory of the
+ * [P1] "정리" comparison table is the L output itself). Calls are reentrant and
+ * thread-safe. No C++ exception crosses this boundary.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                                 */
+  FA_ERR_SHAPE = -2,       /* B, H, N or d < 1; scale not finite; sizes overflow          */
+  FA_ERR_UNSUPPORTED = -3, /* d > 128, or an unknown dtype code                           */
+  FA_ERR_ALIAS = -4,       /* o or lse overlaps q, k, v, or each other                    */
+  FA_ERR_ALIGN = -5,       /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned   */
+  FA_ERR_HIP = -6          /* the HIP runtime refused the launch; see fa_last_hip_error() */
+};
+
+/* dtype codes for fa_fwd_supported(). */
+enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
+
+/*
+ * fa_fwd — exact attention forward in the FA2 loop order, bfloat16 tensors.
+ *
+ * Computes, for every batch b < B, head h < H and query row i < N
+ * ([P1] "왜 필요한가" problem statement; [P2] tiling pseudocode and
+ * [P3] "N×N 행렬은 꼭 저장해야 할까" for the 1/sqrt(d)-style scale):
+ *
+ *   S_ij   = scale * sum_c Q[b,h,i,c] * K[b,h,j,c]      over allowed keys j
+ *   P_ij   = exp(S_ij) / sum_j' exp(S_ij')                ([P1] softmax equation)
+ *   O[b,h,i,:] = sum_j P_ij * V[b,h,j,:]
+ *   lse[b,h,i] = log sum_j exp(S_ij)                       ([P1] FA2 section,
+ *                                                           epilogue equation L = m + log l)
+ *
+ * A key j is allowed when j < N and, if causal != 0, j <= i (the lower-
+ * triangular mask of [P2] "v2와 v3", under which whole key blocks above the
+ * diagonal are skipped). lse is the natural logarithm of the scaled, masked
+ * scores, so that exp(S_ij - lse_i) = P_ij as in the [P1] LSE identity.
+ *
+ * The work follows the [P1] FA2 section: the query row block is the outer
+ * loop and key/value blocks the inner loop; each row keeps a running max m
+ * and sum l on chip, rescales its unnormalised output by exp(m_old - m_new)
+ * only, and divides by l once at the end. S and P never reach device memory.
+ *
+ * Arguments
+ *   q, k, v  device pointers to contiguous row-major [B, H, N, d] bfloat16
+ *            tensors (read only; they may alias each other). 16-byte aligned.
+ *   o        device pointer to a contiguous row-major [B, H, N, d] bfloat16
+ *            output, written with round-to-nearest-even. 16-byte aligned.
+ *   lse      device pointer to a contiguous [B, H, N] float32 output. 4-byte aligned.
+ *   B, H, N  batch, heads and sequence length (queries and keys), each >= 1.
+ *   d        head dimension, 1 <= d <= 128. d = 64 and d = 128 take the fast
+ *            path; any other d takes a bounds-checked path with zero-filled
+ *            columns (same results, slower).
+ *   scale    multiplier of the dot products; any finite value (the usual
+ *            choice is 1/sqrt(d)).
+ *   causal   0 for full attention, nonzero for the causal mask above.
+ *   stream   a hipStream_t passed as void*; NULL means the default stream.
+ *
+ * Ownership: the caller allocates and frees all five buffers; o and lse must
+ * not overlap q, k, v or each other. Totals must satisfy N*d < 2^31 and
+ * B*H*N*d*2 bytes < 2^62.
+ *
+ * Errors: all validation happens on the host before any HIP call, so an
+ * invalid call touches no device state and returns one of FA_ERR_NULL,
+ * FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIAS or FA_ERR_ALIGN. A launch the
+ * runtime refuses returns FA_ERR_HIP and records the hipError_t for
+ * fa_last_hip_error() on the calling thread.
+ *
+ * Asynchrony: the call only enqueues the kernel on `stream` and returns;
+ * faults inside the kernel surface at the caller's next synchronisation.
+ * Non-finite inputs give unspecified (non-finite) outputs.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_fp16 — the same operation, arguments and contract as fa_fwd, for
+ * IEEE float16 q, k, v and o (lse stays float32).
+ */
+int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_supported — 1 if a call with this head dimension, dtype code
+ * (FA_DTYPE_BF16 / FA_DTYPE_FP16) and mask (causal 0/1) is supported, else 0.
+ * The support question is the one [P3] "실제로 적용한다면 먼저 재볼 것"
+ * asks before adopting an implementation (dtype, head dim, mask). Pure host
+ * function; never touches the device.
+ */
+int fa_fwd_supported(int d, int dtype, int causal);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* fa_strerror(int status);
+
+/* The hipError_t (as int) behind the last FA_ERR_HIP on this thread, else 0. */
+int fa_last_hip_error(void);
+
+/* Library version string (static storage). */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

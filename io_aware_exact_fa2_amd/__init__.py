@@ -1,0 +1,161 @@
+"""FA2-order exact attention forward for AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/fa.h`` (``libfa.so``, built from
+``csrc/`` by ``build.py``). It only marshals arguments: every step of the
+computation runs in the HIP kernel. PyTorch supplies device buffers and the
+stream. There is no fallback: if the library is missing, every call raises.
+
+Functions with the C names (``fa_fwd``, ``fa_fwd_fp16``, ``fa_fwd_supported``,
+``fa_strerror``, ``fa_last_hip_error``, ``fa_version``) map 1:1 onto the C
+entry points; ``forward`` is the tensor-level convenience that allocates O and
+L and raises ``FAError`` on a nonzero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIAS",
+    "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError",
+    "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_supported", "fa_strerror",
+    "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
+]
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_UNSUPPORTED = -3
+FA_ERR_ALIAS = -4
+FA_ERR_ALIGN = -5
+FA_ERR_HIP = -6
+FA_DTYPE_BF16 = 0
+FA_DTYPE_FP16 = 1
+
+EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_supported", "fa_strerror",
+           "fa_last_hip_error", "fa_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str = "fa_fwd"):
+        self.status = status
+        msg = f"{where} failed: {status} ({fa_strerror(status)})"
+        if status == FA_ERR_HIP:
+            msg += f", hipError {fa_last_hip_error()}"
+        super().__init__(msg)
+
+
+def library_path() -> str:
+    return os.environ.get("FA355_LIB", os.path.join(_HERE, "libfa.so"))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so once. Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m io_aware_exact_fa2_amd.build` "
+            "(there is no CPU fallback)")
+    L = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    for name in ("fa_fwd", "fa_fwd_fp16"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        fn.restype = i
+    L.fa_fwd_supported.argtypes = [i, i, i]
+    L.fa_fwd_supported.restype = i
+    L.fa_strerror.argtypes = [i]
+    L.fa_strerror.restype = ctypes.c_char_p
+    L.fa_last_hip_error.argtypes = []
+    L.fa_last_hip_error.restype = i
+    L.fa_version.argtypes = []
+    L.fa_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None or isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
+    """C ``fa_fwd`` (bfloat16). Pointers may be tensors or raw integers."""
+    return lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                        float(scale), int(causal), _stream(stream))
+
+
+def fa_fwd_fp16(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
+    """C ``fa_fwd_fp16`` (float16). Pointers may be tensors or raw integers."""
+    return lib().fa_fwd_fp16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                             float(scale), int(causal), _stream(stream))
+
+
+def fa_fwd_supported(d: int, dtype: int, causal: int) -> int:
+    return lib().fa_fwd_supported(d, dtype, causal)
+
+
+def fa_strerror(status: int) -> str:
+    return lib().fa_strerror(status).decode()
+
+
+def fa_last_hip_error() -> int:
+    return lib().fa_last_hip_error()
+
+
+def fa_version() -> str:
+    return lib().fa_version().decode()
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None,
+            out=None, lse=None, stream=None):
+    """O, L for contiguous [B, H, N, d] bf16/fp16 CUDA tensors q, k, v.
+
+    scale defaults to 1/sqrt(d). O has q's dtype; L is float32 [B, H, N]. The
+    launch goes on ``stream`` (default: the current stream of q's device).
+    """
+    import torch
+
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("q, k, v must share dtype bfloat16 or float16")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have the same [B, H, N, d] shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_fp16
+    with torch.cuda.device(q.device):
+        st = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+    if st != FA_OK:
+        raise FAError(st, fn.__name__)
+    return out, lse

@@ -1,0 +1,120 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry point
+include/fa.h declares, and rejects invalid arguments on the host before any HIP
+call (so these calls never touch a device; the fake addresses below are never
+dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import io_aware_exact_fa2_amd as fa
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(fa.library_path()):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return fa.lib()
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_strerror_and_version(L):
+    for code in (fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_UNSUPPORTED,
+                 fa.FA_ERR_ALIAS, fa.FA_ERR_ALIGN, fa.FA_ERR_HIP):
+        assert fa.fa_strerror(code) and fa.fa_strerror(code) != "unknown status"
+    assert fa.fa_strerror(12345) == "unknown status"
+    assert "gfx950" in fa.fa_version()
+    assert fa.fa_last_hip_error() == 0
+
+
+def test_supported_query(L):
+    for d in (1, 4, 63, 64, 65, 127, 128):
+        for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16):
+            for c in (0, 1):
+                assert fa.fa_fwd_supported(d, dt, c) == 1
+    assert fa.fa_fwd_supported(0, 0, 0) == 0
+    assert fa.fa_fwd_supported(129, 0, 0) == 0
+    assert fa.fa_fwd_supported(64, 2, 0) == 0
+
+
+# Fake, never-dereferenced device addresses: far apart, 256-byte aligned.
+QA, KA, VA, OA, LA = (0x7f0000000000 + i * 0x100000000 for i in range(5))
+GOOD = dict(B=2, H=3, N=100, d=64, scale=0.125, causal=0)
+
+
+def _call(fn, q=QA, k=KA, v=VA, o=OA, lse=LA, **kw):
+    a = dict(GOOD, **kw)
+    return fn(q, k, v, o, lse, a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_fp16])
+def test_validation_errors(L, fn):
+    assert _call(fn, q=0) == fa.FA_ERR_NULL
+    assert _call(fn, k=0) == fa.FA_ERR_NULL
+    assert _call(fn, v=0) == fa.FA_ERR_NULL
+    assert _call(fn, o=0) == fa.FA_ERR_NULL
+    assert _call(fn, lse=0) == fa.FA_ERR_NULL
+    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(B=-1), dict(N=-5)):
+        assert _call(fn, **bad) == fa.FA_ERR_SHAPE, bad
+    for s in (float("nan"), float("inf"), float("-inf")):
+        assert _call(fn, scale=s) == fa.FA_ERR_SHAPE
+    assert _call(fn, d=129) == fa.FA_ERR_UNSUPPORTED
+    assert _call(fn, d=100000) == fa.FA_ERR_UNSUPPORTED
+    # N*d must stay below 2^31
+    assert _call(fn, N=2 ** 24, d=128) == fa.FA_ERR_SHAPE
+    # grid limit
+    assert _call(fn, B=2 ** 20, H=2 ** 10, N=1024) == fa.FA_ERR_SHAPE
+    # alignment
+    assert _call(fn, q=QA + 8) == fa.FA_ERR_ALIGN
+    assert _call(fn, o=OA + 2) == fa.FA_ERR_ALIGN
+    assert _call(fn, lse=LA + 2) == fa.FA_ERR_ALIGN
+    # aliasing of outputs with inputs or each other
+    tbytes = GOOD["B"] * GOOD["H"] * GOOD["N"] * GOOD["d"] * 2
+    assert _call(fn, o=QA) == fa.FA_ERR_ALIAS
+    assert _call(fn, o=KA + 16 * ((tbytes - 16) // 16)) == fa.FA_ERR_ALIAS
+    assert _call(fn, lse=VA + 64) == fa.FA_ERR_ALIAS
+    assert _call(fn, lse=OA + tbytes - 16) == fa.FA_ERR_ALIAS
+    # no HIP call was made by any of the above
+    assert fa.fa_last_hip_error() == 0
+
+
+def test_inputs_may_alias_each_other(L):
+    """q, k, v are read-only and may share memory; that is not an alias error.
+    Checked through validation only: with o aliasing q the call must still
+    fail as ALIAS, proving the q/k/v equality did not short-circuit checks."""
+    assert _call(fa.fa_fwd, k=QA, v=QA, o=QA) == fa.FA_ERR_ALIAS
+
+
+def test_forward_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 8, 8, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        fa.forward(x, x, x)
+    y = torch.zeros(1, 1, 8, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(y, y, y)  # CPU tensors are refused before any library call
+    with pytest.raises(ValueError):
+        fa.forward(y, y, torch.zeros(1, 1, 8, 4, dtype=torch.bfloat16))
