@@ -23,15 +23,15 @@ if ROOT not in sys.path:
 METRIC = "FA fwd TFLOPS (4·B·H·N²·d, causal halved) and % of bf16 MFMA peak, 1 GPU"
 PEAK_TFLOPS = 2500.0        # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-KERNEL_SOURCES = ("io_aware_exact_fa2_amd/csrc/fa_fwd_kernel.hpp",
-                  "io_aware_exact_fa2_amd/csrc/fa_fwd.hip")
+CSRC = os.path.join(ROOT, "io_aware_exact_fa2_amd", "csrc")
 
 
 def kernel_hash() -> str:
+    """Short hash of every HIP source file (identifies the kernel a profile was taken on)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

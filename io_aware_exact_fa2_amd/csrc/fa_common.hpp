@@ -1,0 +1,117 @@
+// fa_common.hpp — types and helpers shared by the attention forward kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int N;          // sequence length
+  int d;          // true head dim (row stride of q, k, v, o)
+  int BH;         // B * H
+  int n_qt;       // query tiles per head
+  float c;        // |scale| * log2(e)
+  uint32_t qsign; // 0x80008000 when scale < 0: Q is negated on load (exact), else 0
+  int xcd_map;    // 1 when BH % 8 == 0: the heads of one XCD stay on it
+};
+
+// --- element type -----------------------------------------------------------------
+template <bool BF16> struct Elt;
+template <> struct Elt<true> {
+  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+  // round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2_t x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+  }
+  // acc + lo + hi of a packed pair (v_dot2c_f32_bf16 against (1, 1))
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+  }
+};
+template <> struct Elt<false> {
+  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  // round-to-nearest-even pack of two floats (v_cvt_pk_f16_f32)
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2_t x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
+  }
+  // acc + lo + hi of a packed pair (v_dot2c_f32_f16 against (1, 1))
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w),
+                                  __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
+  }
+};
+
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// MFMA row m of the S^T product holds key rho(m) of the 32-key block: bits 2 and 3 swapped.
+__device__ __forceinline__ int key_of_row(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// Key (within the 32-key block) held by accumulator register r of lane-half h.
+__device__ __forceinline__ constexpr int key_of_reg(int r, int h) { return r + 8 * h + (r & 8); }
+// Reductions across the two wave halves (lane l and lane l^32 hold the same query
+// row): one v_permlane32_swap, which leaves {x[l], x[l^32]} in the two results of
+// every lane, in the same order on both halves (so both halves get equal bits).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                   __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)pr[0]),
+                         __builtin_bit_cast(float, (uint32_t)pr[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                   __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
+}
+
+// Workgroup -> (head, query tile). Workgroups are dispatched round-robin over the
+// 8 XCDs (bid % 8). When the head count allows, all query tiles of a head run on
+// one XCD so its K and V stay in that XCD's L2; causal grids issue the longest
+// (last) query tiles first so the short ones fill the tail.
+template <bool CAUSAL>
+__device__ __forceinline__ void decode_tile(const Params& p, int bid, int& bh, int& qt) {
+  if (p.xcd_map) {
+    const int xcd = bid & 7, s = bid >> 3, hpx = p.BH >> 3;
+    if (CAUSAL) {
+      qt = p.n_qt - 1 - s / hpx;
+      bh = (s % hpx) * 8 + xcd;
+    } else {
+      bh = xcd * hpx + s / p.n_qt;
+      qt = s % p.n_qt;
+    }
+  } else if (CAUSAL) {
+    qt = p.n_qt - 1 - bid / p.BH;
+    bh = bid % p.BH;
+  } else {
+    bh = bid / p.n_qt;
+    qt = bid % p.n_qt;
+  }
+}
+
+}  // namespace fa

@@ -1,7 +1,8 @@
 // fa_fwd.hip — host side of the C ABI declared in include/fa.h: argument
 // validation (entirely before any HIP call), kernel selection and launch.
 #include "fa.h"
-#include "fa_fwd_kernel.hpp"
+#include "fa_fwd_fast.hpp"
+#include "fa_fwd_generic.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -13,9 +14,32 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kNW = 4;   // waves per workgroup
-constexpr int kQB = 1;   // 32-query blocks per wave
-constexpr int kBC = 64;  // keys per tile
+// Launch shapes. The fast path (d = 64, 128) is tunable at build time for sweeps;
+// the defaults are the measured best. The generic path (other d) is fixed.
+#ifndef FA_FAST_NW
+#define FA_FAST_NW 4      // waves per workgroup
+#endif
+#ifndef FA_FAST_QB
+#define FA_FAST_QB 1      // 32-query blocks per wave
+#endif
+#ifndef FA_FAST_BC
+#define FA_FAST_BC 64     // keys per tile
+#endif
+#ifndef FA_TAU
+#define FA_TAU 0          // lazy-rescale threshold in log2 units (0: every tile)
+#endif
+#ifndef FA_WPE_D128
+#define FA_WPE_D128 2     // waves per SIMD the d = 128 kernel is register-limited to
+#endif
+#ifndef FA_WPE_D64
+#define FA_WPE_D64 2
+#endif
+constexpr int kFNW = FA_FAST_NW, kFQB = FA_FAST_QB, kFBC = FA_FAST_BC;
+constexpr int kFBR = kFNW * kFQB * 32;   // queries per workgroup, fast path
+constexpr int kNW = 4;                    // generic path: waves per workgroup
+constexpr int kQB = 1;                    //               32-query blocks per wave
+constexpr int kBC = 64;                   //               keys per tile
+constexpr int kGBR = kNW * kQB * 32;      //               queries per workgroup
 
 bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
@@ -36,7 +60,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   const int64_t rows = bh * N;                       // < 2^62
   if (rows > (int64_t(1) << 54)) return FA_ERR_SHAPE;
   const int64_t elems = rows * d;                    // < 2^61
-  const int64_t n_qt = (N + kNW * kQB * 32 - 1) / (kNW * kQB * 32);
+  const int64_t min_br = kFBR < kGBR ? kFBR : kGBR;
+  const int64_t n_qt = (N + min_br - 1) / min_br;
   if (n_qt * bh >= (int64_t(1) << 31) / 64) return FA_ERR_SHAPE;   // grid limit
   const uint64_t tbytes = static_cast<uint64_t>(elems) * 2u;
   const uint64_t lbytes = static_cast<uint64_t>(rows) * 4u;
@@ -51,9 +76,21 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
-template <bool BF16, int D, bool EXACT_D, bool CAUSAL>
-hipError_t launch_one(const fa::Params& p, int grid, hipStream_t stream) {
-  auto kern = fa::fa_fwd_kernel<BF16, D, EXACT_D, CAUSAL, kQB, kNW, kBC>;
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_fast(fa::Params p, hipStream_t stream) {
+  constexpr int WPE = D == 128 ? FA_WPE_D128 : FA_WPE_D64;
+  p.n_qt = (p.N + kFBR - 1) / kFBR;
+  const int grid = p.n_qt * p.BH;
+  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFQB, kFNW, kFBC, FA_TAU, WPE>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_generic(fa::Params p, hipStream_t stream) {
+  p.n_qt = (p.N + kGBR - 1) / kGBR;
+  const int grid = p.n_qt * p.BH;
+  auto kern = fa::fa_fwd_generic_kernel<BF16, D, false, CAUSAL, kQB, kNW, kBC>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kNW * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -64,7 +101,6 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   const int st = validate(q, k, v, o, lse, B, H, N, d, scale);
   if (st != FA_OK) return st;
 
-  constexpr int BR = kNW * kQB * 32;
   fa::Params p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -74,26 +110,22 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   p.N = N;
   p.d = d;
   p.BH = B * H;
-  p.n_qt = (N + BR - 1) / BR;
+  p.n_qt = 0;  // set per launch shape
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
   p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
-  const int grid = p.n_qt * p.BH;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;
   const bool cz = causal != 0;
-  if (d <= 64) {
-    if (d == 64) e = cz ? launch_one<BF16, 64, true, true>(p, grid, s)
-                        : launch_one<BF16, 64, true, false>(p, grid, s);
-    else e = cz ? launch_one<BF16, 64, false, true>(p, grid, s)
-                : launch_one<BF16, 64, false, false>(p, grid, s);
-  } else {
-    if (d == 128) e = cz ? launch_one<BF16, 128, true, true>(p, grid, s)
-                         : launch_one<BF16, 128, true, false>(p, grid, s);
-    else e = cz ? launch_one<BF16, 128, false, true>(p, grid, s)
-                : launch_one<BF16, 128, false, false>(p, grid, s);
-  }
+  // scale == 0 (every allowed score equal) takes the generic kernel, which zeroes
+  // masked probabilities explicitly; the fast kernel relies on exp2(-inf * c) = 0, c > 0.
+  const bool fast = (d == 128 || d == 64) && p.c > 0.f;
+  if (!fast) {
+    if (d <= 64) e = cz ? launch_generic<BF16, 64, true>(p, s) : launch_generic<BF16, 64, false>(p, s);
+    else e = cz ? launch_generic<BF16, 128, true>(p, s) : launch_generic<BF16, 128, false>(p, s);
+  } else if (d == 128) e = cz ? launch_fast<BF16, 128, true>(p, s) : launch_fast<BF16, 128, false>(p, s);
+  else e = cz ? launch_fast<BF16, 64, true>(p, s) : launch_fast<BF16, 64, false>(p, s);
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return FA_ERR_HIP;

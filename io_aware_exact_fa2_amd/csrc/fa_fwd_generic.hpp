@@ -1,4 +1,5 @@
-// fa_fwd_kernel.hpp — FA2-order attention forward for gfx950 (MI355X), HIP device code.
+// fa_fwd_generic.hpp — FA2-order attention forward for gfx950 (MI355X): the generic
+// kernel, used for head dims other than 64 and 128 (bounds-checked, zero-filled columns).
 //
 // Algorithm ([P1] currybab.bearblog.dev, "Triton으로 FlashAttention 구현하기 전에 -
 // FA1, 2 forward pass", section "FlashAttention 2 forward pass 알고리즘 분석"):
@@ -36,63 +37,13 @@
 //     applied only on diagonal and ragged-tail tiles.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "fa_common.hpp"
 
 namespace fa {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-struct Params {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  float* lse;
-  int N;          // sequence length
-  int d;          // true head dim (row stride of q, k, v, o)
-  int BH;         // B * H
-  int n_qt;       // query tiles per head
-  float c;        // |scale| * log2(e)
-  uint32_t qsign; // 0x80008000 when scale < 0: Q is negated on load (exact), else 0
-  int xcd_map;    // 1 when BH % 8 == 0: the heads of one XCD stay on it
-};
-
-// --- element type -----------------------------------------------------------------
-template <bool BF16> struct Elt;
-template <> struct Elt<true> {
-  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-  }
-  // round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    f32x2_t x = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
-  }
-};
-template <> struct Elt<false> {
-  static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-  }
-  // round-to-nearest-even pack of two floats (v_cvt_pk_f16_f32)
-  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-    f32x2_t x = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2_t));
-  }
-};
-
 // --- tile geometry ----------------------------------------------------------------
 template <int D_, int QB_, int NW_, int BC_>
-struct Geom {
+struct GenericGeom {
   static constexpr int D = D_;      // padded head dim: 64 or 128
   static constexpr int QB = QB_;    // 32-query blocks per wave
   static constexpr int NW = NW_;    // waves per workgroup
@@ -115,19 +66,9 @@ struct Geom {
   static_assert(BC / KCH * CPR == NT, "V transposing loader covers the tile exactly");
 };
 
-// MFMA row m of the S^T product holds key rho(m) of the 32-key block: bits 2 and 3 swapped.
-__device__ __forceinline__ int key_of_row(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-// Key (within the 32-key block) held by accumulator register r of lane-half h.
-__device__ __forceinline__ constexpr int key_of_reg(int r, int h) { return r + 8 * h + (r & 8); }
 // XOR swizzle of the 16-byte key units of V^T row `dcol` (conflict-free b128 reads
 // along consecutive rows, at most 2-way conflicts on the b64 transposing writes).
 __device__ __forceinline__ int vt_swz(int dcol) { return ((dcol >> 1) ^ (dcol >> 4)) & 7; }
-
-__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
 
 // Bounds-checked 8-element load for head dims that are not the padded size.
 __device__ __forceinline__ u32x4_t ld8_ragged(const uint16_t* row, int col, int d) {
@@ -144,8 +85,8 @@ __device__ __forceinline__ u32x4_t ld8_ragged(const uint16_t* row, int col, int 
 
 template <bool BF16, int D, bool EXACT_D, bool CAUSAL, int QB, int NW, int BC>
 __global__ void __launch_bounds__(NW * 64)
-fa_fwd_kernel(const Params p) {
-  using G = Geom<D, QB, NW, BC>;
+fa_fwd_generic_kernel(const Params p) {
+  using G = GenericGeom<D, QB, NW, BC>;
   using E = Elt<BF16>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::LDS];
 
@@ -158,27 +99,8 @@ fa_fwd_kernel(const Params p) {
   const int dstride = EXACT_D ? D : p.d;
 
   // ---- workgroup -> (head, query tile) -------------------------------------------
-  // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). When the head
-  // count allows, all query tiles of a head run on one XCD so its K/V stay in that
-  // XCD's L2; causal grids issue the longest (last) query tiles first.
-  const int bid = blockIdx.x;
   int bh, qt;
-  if (p.xcd_map) {
-    const int xcd = bid & 7, s = bid >> 3, hpx = p.BH >> 3;
-    if (CAUSAL) {
-      qt = p.n_qt - 1 - s / hpx;
-      bh = (s % hpx) * 8 + xcd;
-    } else {
-      bh = xcd * hpx + s / p.n_qt;
-      qt = s % p.n_qt;
-    }
-  } else if (CAUSAL) {
-    qt = p.n_qt - 1 - bid / p.BH;
-    bh = bid % p.BH;
-  } else {
-    bh = bid / p.n_qt;
-    qt = bid % p.n_qt;
-  }
+  decode_tile<CAUSAL>(p, blockIdx.x, bh, qt);
   const size_t head = (size_t)bh * (size_t)N * (size_t)dstride;
   const uint16_t* __restrict__ qg = p.q + head;
   const uint16_t* __restrict__ kg = p.k + head;
