@@ -31,8 +31,13 @@ enum fa_status {
   FA_ERR_HIP = -6          /* the HIP runtime refused the launch; see fa_last_hip_error() */
 };
 
-/* dtype codes for fa_fwd_supported(). */
+/* dtype codes for fa_fwd_ex() and fa_fwd_supported(). */
 enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
+
+/* Rescale threshold of fa_fwd / fa_fwd_fp16, and the largest one fa_fwd_ex accepts
+ * (log2 units; see fa_fwd_ex). */
+#define FA_DEFAULT_RESCALE_LOG2 8.0f
+#define FA_MAX_RESCALE_LOG2 15.0f
 
 /*
  * fa_fwd — exact attention forward in the FA2 loop order, bfloat16 tensors.
@@ -95,6 +100,28 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_ex — fa_fwd / fa_fwd_fp16 with the dtype as an argument (FA_DTYPE_BF16 or
+ * FA_DTYPE_FP16; anything else returns FA_ERR_UNSUPPORTED) and an explicit rescale
+ * threshold.
+ *
+ * The running-max update of the [P1] FA2 section (m_new = max(m_old, rowmax S),
+ * alpha = exp(m_old - m_new) applied to l and the unnormalised O) is taken on a key
+ * block only when some row's block max exceeds its current reference by more than
+ * rescale_log2 (in log2 units, i.e. a factor 2^rescale_log2); otherwise the row
+ * keeps the old reference and that block's probabilities may reach 2^rescale_log2.
+ * The softmax is unchanged by the choice of reference (the max shift cancels, as the
+ * [P1] "Online Softmax 개념" block form shows), so O and lse are the same up to
+ * rounding for every threshold. rescale_log2 = 0 is the literal per-block update of
+ * the pages. 0 <= rescale_log2 <= FA_MAX_RESCALE_LOG2 (which keeps float16
+ * probabilities finite), else FA_ERR_SHAPE. fa_fwd and fa_fwd_fp16 use
+ * FA_DEFAULT_RESCALE_LOG2. Head dims other than 64 and 128, and scale = 0, always
+ * take the per-block update.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int d, float scale, int causal, int dtype,
+              float rescale_log2, void* stream);
 
 /*
  * fa_fwd_supported — 1 if a call with this head dimension, dtype code

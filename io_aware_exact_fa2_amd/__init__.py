@@ -19,7 +19,8 @@ import os
 __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIAS",
     "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError",
-    "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_supported", "fa_strerror",
+    "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
+    "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
 ]
 
@@ -33,8 +34,10 @@ FA_ERR_HIP = -6
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_supported", "fa_strerror",
+EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported", "fa_strerror",
            "fa_last_hip_error", "fa_version")
+FA_DEFAULT_RESCALE_LOG2 = 8.0
+FA_MAX_RESCALE_LOG2 = 15.0
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -69,6 +72,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         fn.restype = i
+    L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, vp]
+    L.fa_fwd_ex.restype = i
     L.fa_fwd_supported.argtypes = [i, i, i]
     L.fa_fwd_supported.restype = i
     L.fa_strerror.argtypes = [i]
@@ -107,6 +112,14 @@ def fa_fwd_fp16(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None) -> int:
                              float(scale), int(causal), _stream(stream))
 
 
+def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, rescale_log2,
+              stream=None) -> int:
+    """C ``fa_fwd_ex``: explicit dtype code and rescale threshold (log2 units)."""
+    return lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                           float(scale), int(causal), int(dtype), float(rescale_log2),
+                           _stream(stream))
+
+
 def fa_fwd_supported(d: int, dtype: int, causal: int) -> int:
     return lib().fa_fwd_supported(d, dtype, causal)
 
@@ -124,11 +137,13 @@ def fa_version() -> str:
 
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None,
-            out=None, lse=None, stream=None):
+            out=None, lse=None, stream=None, rescale_log2: float | None = None):
     """O, L for contiguous [B, H, N, d] bf16/fp16 CUDA tensors q, k, v.
 
     scale defaults to 1/sqrt(d). O has q's dtype; L is float32 [B, H, N]. The
     launch goes on ``stream`` (default: the current stream of q's device).
+    rescale_log2 selects the running-max rescale threshold (``fa_fwd_ex``); None
+    uses the library default (``fa_fwd`` / ``fa_fwd_fp16``).
     """
     import torch
 
@@ -153,9 +168,16 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_fp16
     with torch.cuda.device(q.device):
-        st = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+        if rescale_log2 is None:
+            fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_fp16
+            st = fn(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+            name = fn.__name__
+        else:
+            dt = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else FA_DTYPE_FP16
+            st = fa_fwd_ex(q, k, v, out, lse, B, H, N, d, scale, causal, dt, rescale_log2,
+                           stream)
+            name = "fa_fwd_ex"
     if st != FA_OK:
-        raise FAError(st, fn.__name__)
+        raise FAError(st, name)
     return out, lse

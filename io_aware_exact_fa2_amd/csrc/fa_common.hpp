@@ -28,6 +28,7 @@ struct Params {
   float c;        // |scale| * log2(e)
   uint32_t qsign; // 0x80008000 when scale < 0: Q is negated on load (exact), else 0
   int xcd_map;    // 1 when BH % 8 == 0: the heads of one XCD stay on it
+  float tau;      // rescale threshold in log2 units (fast kernel; 0: every tile)
 };
 
 // --- element type -----------------------------------------------------------------

@@ -17,16 +17,19 @@ thread_local int g_last_hip_error = 0;
 // Launch shapes. The fast path (d = 64, 128) is tunable at build time for sweeps;
 // the defaults are the measured best. The generic path (other d) is fixed.
 #ifndef FA_FAST_NW
-#define FA_FAST_NW 4      // waves per workgroup
+#define FA_FAST_NW 8      // waves per workgroup
 #endif
-#ifndef FA_FAST_QB
-#define FA_FAST_QB 1      // 32-query blocks per wave
+#ifndef FA_QB_D128
+#define FA_QB_D128 1      // 32-query blocks per wave at d = 128
 #endif
-#ifndef FA_FAST_BC
-#define FA_FAST_BC 64     // keys per tile
+#ifndef FA_QB_D64
+#define FA_QB_D64 1       // 32-query blocks per wave at d = 64
 #endif
-#ifndef FA_TAU
-#define FA_TAU 0          // lazy-rescale threshold in log2 units (0: every tile)
+#ifndef FA_BC_D128
+#define FA_BC_D128 64     // keys per tile at d = 128
+#endif
+#ifndef FA_BC_D64
+#define FA_BC_D64 64      // keys per tile at d = 64
 #endif
 #ifndef FA_WPE_D128
 #define FA_WPE_D128 2     // waves per SIMD the d = 128 kernel is register-limited to
@@ -34,12 +37,12 @@ thread_local int g_last_hip_error = 0;
 #ifndef FA_WPE_D64
 #define FA_WPE_D64 2
 #endif
-constexpr int kFNW = FA_FAST_NW, kFQB = FA_FAST_QB, kFBC = FA_FAST_BC;
-constexpr int kFBR = kFNW * kFQB * 32;   // queries per workgroup, fast path
+constexpr int kFNW = FA_FAST_NW;
 constexpr int kNW = 4;                    // generic path: waves per workgroup
 constexpr int kQB = 1;                    //               32-query blocks per wave
 constexpr int kBC = 64;                   //               keys per tile
 constexpr int kGBR = kNW * kQB * 32;      //               queries per workgroup
+constexpr int kMinBR = kFNW * 32 < kGBR ? kFNW * 32 : kGBR;   // smallest query tile
 
 bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
@@ -48,10 +51,11 @@ bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
 }
 
 int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
-             int B, int H, int N, int d, float scale) {
+             int B, int H, int N, int d, float scale, float tau) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_SHAPE;
   if (!std::isfinite(scale)) return FA_ERR_SHAPE;
+  if (!(tau >= 0.f && tau <= FA_MAX_RESCALE_LOG2)) return FA_ERR_SHAPE;
   if (d > 128) return FA_ERR_UNSUPPORTED;
   // N*d indexes one head with 32-bit row arithmetic; B*H*N*d*2 bytes must be addressable
   if (static_cast<int64_t>(N) * d >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
@@ -60,8 +64,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
   const int64_t rows = bh * N;                       // < 2^62
   if (rows > (int64_t(1) << 54)) return FA_ERR_SHAPE;
   const int64_t elems = rows * d;                    // < 2^61
-  const int64_t min_br = kFBR < kGBR ? kFBR : kGBR;
-  const int64_t n_qt = (N + min_br - 1) / min_br;
+  const int64_t n_qt = (N + kMinBR - 1) / kMinBR;
   if (n_qt * bh >= (int64_t(1) << 31) / 64) return FA_ERR_SHAPE;   // grid limit
   const uint64_t tbytes = static_cast<uint64_t>(elems) * 2u;
   const uint64_t lbytes = static_cast<uint64_t>(rows) * 4u;
@@ -79,9 +82,12 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_fast(fa::Params p, hipStream_t stream) {
   constexpr int WPE = D == 128 ? FA_WPE_D128 : FA_WPE_D64;
-  p.n_qt = (p.N + kFBR - 1) / kFBR;
+  constexpr int QB = D == 128 ? FA_QB_D128 : FA_QB_D64;
+  constexpr int BC = D == 128 ? FA_BC_D128 : FA_BC_D64;
+  constexpr int BR = kFNW * QB * 32;
+  p.n_qt = (p.N + BR - 1) / BR;
   const int grid = p.n_qt * p.BH;
-  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFQB, kFNW, kFBC, FA_TAU, WPE>;
+  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, QB, kFNW, BC, WPE>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -97,8 +103,8 @@ hipError_t launch_generic(fa::Params p, hipStream_t stream) {
 
 template <bool BF16>
 int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                int N, int d, float scale, int causal, void* stream) {
-  const int st = validate(q, k, v, o, lse, B, H, N, d, scale);
+                int N, int d, float scale, int causal, float tau, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, H, N, d, scale, tau);
   if (st != FA_OK) return st;
 
   fa::Params p;
@@ -114,6 +120,7 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
   p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
+  p.tau = tau;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;
@@ -139,12 +146,24 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int causal, void* stream) {
-  return fa_fwd_impl<true>(q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+  return fa_fwd_impl<true>(q, k, v, o, lse, B, H, N, d, scale, causal,
+                           FA_DEFAULT_RESCALE_LOG2, stream);
 }
 
 int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                 int N, int d, float scale, int causal, void* stream) {
-  return fa_fwd_impl<false>(q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+  return fa_fwd_impl<false>(q, k, v, o, lse, B, H, N, d, scale, causal,
+                            FA_DEFAULT_RESCALE_LOG2, stream);
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int N, int d, float scale, int causal, int dtype, float rescale_log2,
+              void* stream) {
+  if (dtype == FA_DTYPE_BF16)
+    return fa_fwd_impl<true>(q, k, v, o, lse, B, H, N, d, scale, causal, rescale_log2, stream);
+  if (dtype == FA_DTYPE_FP16)
+    return fa_fwd_impl<false>(q, k, v, o, lse, B, H, N, d, scale, causal, rescale_log2, stream);
+  return FA_ERR_UNSUPPORTED;
 }
 
 int fa_fwd_supported(int d, int dtype, int causal) {
@@ -158,7 +177,7 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "invalid shape or scale (B, H, N, d >= 1; finite scale; sizes in range)";
+    case FA_ERR_SHAPE: return "invalid shape, scale or rescale threshold (B, H, N, d >= 1; finite scale; 0 <= threshold <= 15; sizes in range)";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (1 <= d <= 128) or dtype";
     case FA_ERR_ALIAS: return "o or lse overlaps q, k, v or each other";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";

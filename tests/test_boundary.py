@@ -28,6 +28,15 @@ def L():
     return fa.lib()
 
 
+@pytest.fixture
+def no_gpu():
+    """Calls below pass fake device addresses that validation must reject. They run
+    only where no GPU exists, so a validation bug can never reach a real launch."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run on GPU-less hosts only")
+
+
 def test_header_declares_the_boundary():
     assert _declared_functions() == sorted(fa.EXPORTS)
 
@@ -71,7 +80,7 @@ def _call(fn, q=QA, k=KA, v=VA, o=OA, lse=LA, **kw):
 
 
 @pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_fp16])
-def test_validation_errors(L, fn):
+def test_validation_errors(L, no_gpu, fn):
     assert _call(fn, q=0) == fa.FA_ERR_NULL
     assert _call(fn, k=0) == fa.FA_ERR_NULL
     assert _call(fn, v=0) == fa.FA_ERR_NULL
@@ -101,7 +110,22 @@ def test_validation_errors(L, fn):
     assert fa.fa_last_hip_error() == 0
 
 
-def test_inputs_may_alias_each_other(L):
+def test_fa_fwd_ex_validation(L, no_gpu):
+    def ex(dtype=fa.FA_DTYPE_BF16, tau=8.0, q=QA, k=KA, v=VA, o=OA, lse=LA, **kw):
+        a = dict(GOOD, **kw)
+        return fa.fa_fwd_ex(q, k, v, o, lse, a["B"], a["H"], a["N"], a["d"], a["scale"],
+                            a["causal"], dtype, tau, None)
+    assert ex(dtype=2) == fa.FA_ERR_UNSUPPORTED
+    assert ex(dtype=-1) == fa.FA_ERR_UNSUPPORTED
+    for tau in (-0.5, 15.5, 100.0, float("nan"), float("inf")):
+        assert ex(tau=tau) == fa.FA_ERR_SHAPE, tau
+    assert ex(tau=0.0, N=0) == fa.FA_ERR_SHAPE
+    assert ex(tau=fa.FA_MAX_RESCALE_LOG2, o=QA) == fa.FA_ERR_ALIAS
+    assert ex(dtype=fa.FA_DTYPE_FP16, tau=0.0, q=0) == fa.FA_ERR_NULL
+    assert fa.fa_last_hip_error() == 0
+
+
+def test_inputs_may_alias_each_other(L, no_gpu):
     """q, k, v are read-only and may share memory; that is not an alias error.
     Checked through validation only: with o aliasing q the call must still
     fail as ALIAS, proving the q/k/v equality did not short-circuit checks."""

@@ -41,9 +41,9 @@ def _need_gpu():
                 f.write(json.dumps(r) + "\n")
 
 
-def _gpu(q, k, v, causal, scale):
+def _gpu(q, k, v, causal, scale, rescale_log2=None):
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+    o, lse = fa.forward(qd, kd, vd, causal=causal, scale=scale, rescale_log2=rescale_log2)
     torch.cuda.synchronize()
     return o, lse
 
@@ -64,12 +64,13 @@ def _check(name, dtype, o_gpu, l_gpu, o_ref, l_ref):
     assert rec["max_abs_L"] <= TOL_L, rec
 
 
-def _full_case(w: Workload, causal=None, scale=None, q=None, k=None, v=None, name=None):
+def _full_case(w: Workload, causal=None, scale=None, q=None, k=None, v=None, name=None,
+               rescale_log2=None):
     causal = w.causal if causal is None else causal
     scale = w.scale if scale is None else scale
     if q is None:
         q, k, v = workloads.make_inputs(w)
-    o, lse = _gpu(q, k, v, causal, scale)
+    o, lse = _gpu(q, k, v, causal, scale, rescale_log2)
     O, L = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale, causal)
     _check(name or f"{w.name}/{w.B}x{w.H}x{w.N}x{w.d}/causal={causal}", w.dtype,
            to_f64(o), to_f64(lse), O, L)
@@ -165,6 +166,35 @@ def test_head_counts(BH):
     for causal in (False, True):
         w = Workload(f"heads{B}x{H}", B, H, 200, 64, "fp16", causal, seed=4000 + B * H)
         _full_case(w)
+
+
+RESCALE_CASES = [
+    ("ai_small", 1, 4, 700, 128, "bf16", False, "normal"),
+    ("causal_small", 1, 4, 900, 128, "bf16", True, "normal"),
+    ("stress_small", 2, 4, 1000, 64, "fp16", False, "stress"),
+    ("stress_causal", 1, 4, 1000, 128, "fp16", True, "stress"),
+]
+
+
+@pytest.mark.parametrize("tau", [0.0, 3.0, 15.0])
+@pytest.mark.parametrize("case", RESCALE_CASES, ids=[c[0] for c in RESCALE_CASES])
+def test_rescale_threshold(case, tau):
+    """fa_fwd_ex at the literal per-block max update (0), an intermediate and the
+    largest threshold: same results as the oracle; the spiked-key inputs force
+    rescales mid-stream in every mode."""
+    name, B, H, N, d, dt, causal, dist = case
+    w = Workload(name, B, H, N, d, dt, causal, seed=8000 + N + d, dist=dist)
+    _full_case(w, rescale_log2=tau, name=f"{name}/tau={tau}")
+
+
+def test_rescale_threshold_modes_agree():
+    w = workloads.scaled(workloads.get("stress4000"), B=1, H=8)
+    q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
+    outs = [fa.forward(q, k, v, rescale_log2=t) for t in (0.0, 8.0, 15.0)]
+    torch.cuda.synchronize()
+    for o, l in outs[1:]:
+        assert (o.float() - outs[0][0].float()).abs().max().item() <= 2 * TOL_O["fp16"]
+        assert (l - outs[0][1]).abs().max().item() <= TOL_L
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 1.0, 3.0])
