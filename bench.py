@@ -79,6 +79,72 @@ def time_gpu(w, steps, warmup):
     return ms, wall
 
 
+def calibrate_copy(mib: int):
+    """A plain device copy of known size (float32 multiply by 1, out of place) whose
+    FETCH_SIZE / WRITE_SIZE counters calibrate the attention kernel's traffic."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _counter_means(directory, counter):
+    """Mean per-dispatch value of one counter, by kernel name."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
+    HBM bytes per launch of the attention kernel, each counter scaled by what it reads
+    for the plain copy of copy_mib MiB in the same run."""
+    import workloads
+
+    w = workloads.get(workload)
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    fa_name = next(k for k in fetch if "fa_fwd" in k)
+    copy_name = next(k for k in fetch if "MulFunctor" in k)
+    copy_kib = copy_mib * 1024.0
+    f_scale = copy_kib / fetch[copy_name]
+    w_scale = copy_kib / write[copy_name]
+    fa_bytes = (fetch[fa_name] * f_scale + write[fa_name] * w_scale) * 1024.0
+    rec = {
+        "workload": w.name, "kernel": fa_name,
+        "kernel_source_sha256_16": kernel_hash(),
+        "fetch_kib_per_dispatch": fetch[fa_name], "write_kib_per_dispatch": write[fa_name],
+        "copy_mib": copy_mib, "copy_kernel": copy_name,
+        "copy_fetch_kib": fetch[copy_name], "copy_write_kib": write[copy_name],
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_bytes_per_launch": fa_bytes,
+        "algorithmic_bytes_per_launch": w.min_bytes(),
+        "traffic_over_algorithmic": fa_bytes / w.min_bytes(),
+        "commands": commands,
+    }
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def cpu_baseline(w, budget_s: float):
     """The float64 oracle on whole heads of the same workload until ~budget_s."""
     import numpy as np
@@ -93,8 +159,10 @@ def cpu_baseline(w, budget_s: float):
     done = 0
     t0 = time.perf_counter()
     step = max(1, min(len(heads), workers))
-    while done < len(heads):
-        batch = heads[done:done + step]
+    # whole heads (all rows) until the budget is spent; passes repeat if one is shorter
+    while True:
+        i = done % len(heads)
+        batch = heads[i:i + step]
         oracle.attention_rows(qf, kf, vf, w.scale, w.causal, batch, np.arange(w.N),
                               workers=workers)
         done += len(batch)
@@ -103,8 +171,8 @@ def cpu_baseline(w, budget_s: float):
     dt = time.perf_counter() - t0
     flops = w.flops() * done / len(heads)
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": workers, "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (b,h) heads of {w.name}, all {w.N} rows each, "
-                      f"float64 numpy, {dt:.1f} s"}
+            "sample": f"{done} (b,h) heads of {w.name} ({len(heads)} per batch), all {w.N} "
+                      f"rows each, float64 numpy, {dt:.1f} s"}
 
 
 def main(argv=None):
@@ -117,7 +185,18 @@ def main(argv=None):
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--also", default="causal8k,long32k,stress4000",
                     help="extra workloads timed for the 'workloads' field ('' for none)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-hbm", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize two rocprofv3 --pmc runs into profiles/ (no GPU work)")
+    ap.add_argument("--commands", default="", help="commands recorded in the summary")
     a = ap.parse_args(argv)
+    if a.summarize_hbm:
+        out = os.path.join(ROOT, "profiles", f"fa_fwd_{a.workload}_hbm_counters.json")
+        rec = summarize_hbm(a.workload, a.summarize_hbm[0], a.summarize_hbm[1],
+                            a.calibrate_copy_mib, out, a.commands)
+        print(json.dumps(rec))
+        return 0
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {a.gpus}): the attention forward "
               "here is built and timed on a single MI355X; see DESIGN.md for how it would "
@@ -130,6 +209,8 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if a.calibrate_copy_mib:
+        calibrate_copy(a.calibrate_copy_mib)
     w = workloads.get(a.workload)
     ms, wall = time_gpu(w, a.steps, a.warmup)
     tflops = w.flops() / (ms * 1e-3) / 1e12
