@@ -19,12 +19,6 @@ thread_local int g_last_hip_error = 0;
 #ifndef FA_FAST_NW
 #define FA_FAST_NW 8      // waves per workgroup
 #endif
-#ifndef FA_QB_D128
-#define FA_QB_D128 1      // 32-query blocks per wave at d = 128
-#endif
-#ifndef FA_QB_D64
-#define FA_QB_D64 1       // 32-query blocks per wave at d = 64
-#endif
 #ifndef FA_BC_D128
 #define FA_BC_D128 64     // keys per tile at d = 128
 #endif
@@ -82,12 +76,11 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_fast(fa::Params p, hipStream_t stream) {
   constexpr int WPE = D == 128 ? FA_WPE_D128 : FA_WPE_D64;
-  constexpr int QB = D == 128 ? FA_QB_D128 : FA_QB_D64;
   constexpr int BC = D == 128 ? FA_BC_D128 : FA_BC_D64;
-  constexpr int BR = kFNW * QB * 32;
+  constexpr int BR = kFNW * 32;
   p.n_qt = (p.N + BR - 1) / BR;
   const int grid = p.n_qt * p.BH;
-  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, QB, kFNW, BC, WPE>;
+  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, BC, WPE>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
   return hipGetLastError();
 }

@@ -10,21 +10,26 @@
 // end (the section's per-block update and epilogue equations). Waves own disjoint
 // query rows (split-Q), so no cross-wave merge exists.
 //
-// gfx950 mapping (differences from the generic kernel in fa_fwd_generic.hpp):
-//   * K and V tiles are copied HBM -> LDS by global_load_lds_dwordx4 (no register
-//     staging, no VALU work) into two LDS slots each; one barrier per tile. The copy
-//     instructions are spread over the pipeline steps, one per S^T MFMA step, so a
-//     wave never stalls on a burst of them. K runs
-//     one tile ahead of V: while tile j is finished, the S^T MFMAs of tile j+1 are
-//     issued in the same straight-line block as the exponentials of tile j, so the
-//     matrix cores and the VALU work on different tiles at the same time. Both stay row-major in LDS; K rows carry one 16-byte pad chunk and V rows
-//     four, which makes every LDS read below bank-conflict free with compile-time
-//     address offsets (the pad slots are simply not written).
+// gfx950 mapping:
+//   * K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register
+//     staging, no VALU work) into two LDS slots each; one barrier per tile. Each tile
+//     is a whole number of 1 KB wave copies and every wave issues the same number,
+//     with no branches (past the last tile a wave re-copies the last tile into a
+//     slot that is already free), so the copies can be scheduled between MFMAs.
+//   * K runs one tile ahead of V: while tile j is finished, the S^T MFMAs of tile
+//     j+1 are interleaved with the exponentials of tile j, and the P V MFMAs of tile
+//     j with the row max of tile j+1, so the matrix cores and the VALU work on
+//     different tiles at the same time (the order is imposed on the machine
+//     scheduler with sched_group_barrier patterns).
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}: each lane owns
 //     one query column, so the running max/sum and the alpha rescale are in-lane and
 //     the S^T accumulator, rounded to 16 bits, is the B operand of the P V MFMA.
 //     Key rows enter the S^T MFMA with bits 2 and 3 of the row index swapped so a
 //     lane's 8 values of one 16-key step are 8 consecutive keys.
+//   * K and V stay row-major in LDS, with the 16-byte chunks of each row XOR-
+//     swizzled by the row index so every ds_read_b128 of K and every
+//     ds_read_b64_tr_b16 of V is bank-conflict free; the per-lane addresses are
+//     computed once, the per-step offsets are compile-time.
 //   * The V^T operand is read with ds_read_b64_tr_b16: in each 16-lane group, lane i
 //     receives column i of the 4 rows the group loads, i.e. 4 consecutive keys of
 //     one head-dim column; two such reads form one 8-key MFMA operand.
@@ -39,7 +44,7 @@
 //     2^tau. Softmax is invariant to the reference, so O and L are unchanged; tau = 0
 //     is the literal update of every tile, with the multiply skipped when no row of
 //     the wave changed its max (alpha = 1).
-//   * Causal: key tiles past the workgroup's last query are never loaded, a wave
+//   * Causal: key tiles past the workgroup's last query are never computed, a wave
 //     skips tiles past its own last query, and element masks are applied only on
 //     diagonal and ragged-tail tiles ([P2] iq-universe.github.io, "FlashAttention은
 //     어떻게 O(N²) 메모리 벽을 넘었나", section "v2와 v3": blocks above the diagonal
@@ -48,6 +53,19 @@
 
 #include "fa_common.hpp"
 
+// Interleave patterns (instructions per pipeline step) given to the machine scheduler.
+#ifndef FA_SG_B_VALU
+#define FA_SG_B_VALU 7    // VALU per S^T MFMA step (exponentials of the previous tile)
+#endif
+#ifndef FA_SG_C_VALU
+#define FA_SG_C_VALU 2    // VALU per P V MFMA step (row max of the next tile)
+#endif
+#ifndef FA_SG_PREFETCH
+#define FA_SG_PREFETCH 2  // MFMA steps an LDS operand read runs ahead
+#endif
+#ifndef FA_SG_ON
+#define FA_SG_ON 1
+#endif
 
 namespace fa {
 
@@ -55,37 +73,49 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-template <int D_, int QB_, int NW_, int BC_>
+// Word 3 of a raw (stride 0) buffer resource on CDNA: 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+
+// XOR swizzles of the 16-byte chunks of LDS row `row` (K rows, V rows). Both are
+// permutations of a row's chunks; see the bank analysis where they are used.
+template <int D> __device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+template <int D_, int NW_, int BC_>
 struct FastGeom {
   static constexpr int D = D_;
-  static constexpr int QB = QB_;
   static constexpr int NW = NW_;
   static constexpr int BC = BC_;
-  static constexpr int NT = NW * 64;
-  static constexpr int BR = NW * QB * 32;
-  static constexpr int CPR = D / 8;              // 16-byte chunks of data per row
-  static constexpr int KPC = CPR + 1;            // K row pitch in LDS chunks
-  static constexpr int VPC = CPR + 4;            // V row pitch in LDS chunks
-  static constexpr int K_CHUNKS = BC * KPC;
-  static constexpr int V_CHUNKS = BC * VPC;
-  static constexpr int K_INSTR = (K_CHUNKS + 63) / 64;  // 1 KB wave copies per tile
-  static constexpr int V_INSTR = (V_CHUNKS + 63) / 64;
-  static constexpr int K_PER_WAVE = (K_INSTR + NW - 1) / NW;
-  static constexpr int V_PER_WAVE = (V_INSTR + NW - 1) / NW;
-  static constexpr int LDS = 2 * 16 * (K_CHUNKS + V_CHUNKS);
+  static constexpr int BR = NW * 32;             // queries per workgroup (32 per wave)
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int CHUNKS = BC * CPR;        // chunks per K (or V) tile
+  static constexpr int INSTR = CHUNKS / 64;      // 1 KB wave copies per tile and tensor
+  static constexpr int PER_WAVE = INSTR / NW;    // copies per wave per tile and tensor
+  static constexpr int NQK = (BC / 32) * (D / 16);  // S^T MFMA steps per tile
+  static constexpr int NPV = (D / 32) * (BC / 16);  // P V MFMA steps per tile
   static_assert(D == 64 || D == 128, "fast path head dims");
-  static_assert(BC % 32 == 0, "key tiles are whole 32-key MFMA blocks");
+  static_assert(BC % 32 == 0 && CHUNKS % 64 == 0, "whole MFMA blocks and wave copies");
+  static_assert(INSTR % NW == 0 && PER_WAVE >= 1, "every wave issues the same copies");
+  static_assert(2 * PER_WAVE <= NQK, "copies fit in the S^T pipeline steps");
 };
 
-template <bool BF16, int D, bool CAUSAL, int QB, int NW, int BC, int WPE>
+template <bool BF16, int D, bool CAUSAL, int NW, int BC, int WPE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fa_fwd_fast_kernel(const Params p) {
-  using G = FastGeom<D, QB, NW, BC>;
+  using G = FastGeom<D, NW, BC>;
   using E = Elt<BF16>;
-  __shared__ u32x4_t ks0[G::K_CHUNKS];
-  __shared__ u32x4_t vs0[G::V_CHUNKS];
-  __shared__ u32x4_t ks1[G::K_CHUNKS];
-  __shared__ u32x4_t vs1[G::V_CHUNKS];
+  constexpr int CPR = G::CPR, NQK = G::NQK, NPV = G::NPV;
+  constexpr int SPS = (BC / 2) / NQK;  // scores exponentiated per S^T step
+  constexpr int MPS = (BC / 2) / NPV;  // scores max-reduced per P V step
+  static_assert(SPS % 2 == 0 && MPS >= 1, "pipeline step split");
+  __shared__ u32x4_t ks0[G::CHUNKS];
+  __shared__ u32x4_t vs0[G::CHUNKS];
+  __shared__ u32x4_t ks1[G::CHUNKS];
+  __shared__ u32x4_t vs1[G::CHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -102,66 +132,47 @@ fa_fwd_fast_kernel(const Params p) {
   const uint16_t* __restrict__ vg = p.v + head;
 
   const int q0 = qt * G::BR;
-  const int wq0 = q0 + wid * QB * 32;
+  const int wq0 = q0 + wid * 32;
   const int q_end = min(q0 + G::BR, N);
   const int n_kt = CAUSAL ? (q_end + BC - 1) / BC : (N + BC - 1) / BC;
   const bool wave_live = wq0 < N;
-  const int w_last_q = min(wq0 + QB * 32, N) - 1;
+  const int w_last_q = min(wq0 + 32, N) - 1;
   const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
 
-  // ---- per-lane element offsets (within a tile) of the chunks this wave copies ----
-  int koff[G::K_PER_WAVE], voff[G::V_PER_WAVE];
+  // ---- HBM -> LDS copies ---------------------------------------------------------
+  // Lane `lane` of copy instruction i writes LDS chunk 64 i + lane = (row, physical
+  // chunk); it fetches the logical chunk that the swizzle puts there. Element
+  // offsets within a tile are computed once.
+  int koff[G::PER_WAVE], voff[G::PER_WAVE];
 #pragma unroll
-  for (int ii = 0; ii < G::K_PER_WAVE; ++ii) {
-    const int i = wid + ii * NW;
-    const int f = i * 64 + lane, row = f / G::KPC, ch = f % G::KPC;
-    koff[ii] = (f < G::K_CHUNKS && ch < G::CPR) ? row * D + ch * 8 : -1;
+  for (int ii = 0; ii < G::PER_WAVE; ++ii) {
+    const int f = (wid + ii * NW) * 64 + lane, row = f / CPR, ph = f % CPR;
+    koff[ii] = row * D + (ph ^ swz_k<D>(row)) * 8;
+    voff[ii] = row * D + (ph ^ swz_v<D>(row)) * 8;
   }
-#pragma unroll
-  for (int ii = 0; ii < G::V_PER_WAVE; ++ii) {
-    const int i = wid + ii * NW;
-    const int f = i * 64 + lane, row = f / G::VPC, ch = f % G::VPC;
-    voff[ii] = (f < G::V_CHUNKS && ch < G::CPR) ? row * D + ch * 8 : -1;
-  }
-
-  // HBM -> LDS copies of the key (or value) tile j into one LDS slot. Rows past N
-  // are clamped to row N-1 (always a valid address); their scores are masked to
-  // -inf, so their probabilities are exactly 0 and the duplicated values add nothing.
-  auto issue_one = [&](const uint16_t* src, u32x4_t* dst, const int* offs, int n_instr, int ii,
-                       int j) {
-    const int i = wid + ii * NW;
-    if (i < n_instr) {
-      const int k0 = j * BC;
-      int off = offs[ii];
-      if (k0 + BC > N && off >= 0 && k0 + off / D >= N) off = (N - 1 - k0) * D + (off & (D - 1));
-      if (off >= 0)
-        __builtin_amdgcn_global_load_lds(src + (size_t)k0 * D + off, (lds_void_t*)(dst + i * 64),
-                                         16, 0, 0);
-    }
+  // One copy of tile j, as a buffer load with an LDS destination. The buffer resource
+  // spans the tile's rows below N, so chunks of rows past N read as zeros (their
+  // scores are masked to -inf, so they contribute exactly 0). A copy past the last
+  // tile re-fetches the last tile into a slot nobody reads. The buffer form is used
+  // (rather than global_load_lds) because its completion is tracked by vmcnt alone,
+  // so the LDS operand reads of the pipeline keep partial lgkmcnt waits.
+  auto copy = [&](const uint16_t* src, u32x4_t* dst, int off, int ii, int j) {
+    const int k0 = min(j, n_kt - 1) * BC;
+    const int bytes = min(N - k0, BC) * D * 2;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src + (size_t)k0 * D), (short)0, bytes, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (wid + ii * NW) * 64), 16,
+                                             off * 2, 0, 0, 0);
   };
-  auto issue_k = [&](u32x4_t* dst, int j) {
-#pragma unroll
-    for (int ii = 0; ii < G::K_PER_WAVE; ++ii) issue_one(kg, dst, koff, G::K_INSTR, ii, j);
-  };
-  auto issue_v = [&](u32x4_t* dst, int j) {
-#pragma unroll
-    for (int ii = 0; ii < G::V_PER_WAVE; ++ii) issue_one(vg, dst, voff, G::V_INSTR, ii, j);
-  };
-  // The copies of one loop iteration, spread one per pipeline step so that a wave
-  // never stalls on a burst of copy instructions: K tile jk into k_dst (if jk < n_kt)
-  // then V tile jv into v_dst (if jv < n_kt).
-  constexpr int NDMA = G::K_PER_WAVE + G::V_PER_WAVE;
   struct Copies {
     u32x4_t* k_dst;
     u32x4_t* v_dst;
     int jk, jv;
   };
+  constexpr int NDMA = 2 * G::PER_WAVE;
   auto copy_step = [&](const Copies& cp, int i) {
-    if (i < G::K_PER_WAVE) {
-      if (cp.jk < n_kt) issue_one(kg, cp.k_dst, koff, G::K_INSTR, i, cp.jk);
-    } else if (i < NDMA) {
-      if (cp.jv < n_kt) issue_one(vg, cp.v_dst, voff, G::V_INSTR, i - G::K_PER_WAVE, cp.jv);
-    }
+    if (i < G::PER_WAVE) copy(kg, cp.k_dst, koff[i], i, cp.jk);
+    else if (i < NDMA) copy(vg, cp.v_dst, voff[i - G::PER_WAVE], i - G::PER_WAVE, cp.jv);
   };
   auto copy_all = [&](const Copies& cp) {
 #pragma unroll
@@ -169,85 +180,76 @@ fa_fwd_fast_kernel(const Params p) {
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), in registers for the whole loop ------
-  u32x4_t qf[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = wq0 + qb * 32 + l32;
+  u32x4_t qf[D / 16];
+  {
+    const int qi = wq0 + l32;
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
       u32x4_t x = {0u, 0u, 0u, 0u};
       if (qi < N) x = ld16(qg + (size_t)qi * D + ds * 16 + hh * 8);
-      qf[qb][ds] = x ^ p.qsign;
+      qf[ds] = x ^ p.qsign;
     }
   }
 
   // ---- running state ---------------------------------------------------------------
-  f32x16_t oacc[D / 32][QB];
-  float ms[QB], l_part[QB];
+  f32x16_t oacc[D / 32];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    ms[qb] = 0.f;
-    l_part[qb] = 0.f;
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float ms = 0.f, l_part = 0.f;
+  const float c = p.c;
+
+  // ---- per-lane LDS read addresses ---------------------------------------------------
+  // K operand of step (kb, ds): row 32 kb + rho(l32), logical chunk 2 ds + hh. The
+  // swizzle of that row does not depend on kb, so one address per ds (kb adds a
+  // compile-time offset). Bank check: the 16 lanes of a b128 quarter-wave read 16
+  // different rows at one logical chunk; the row-dependent XOR sends them to 16
+  // different bank quads.
+  int kaddr[D / 16];
+  {
+    const int row = key_of_row(l32);
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds)
+      kaddr[ds] = (row * CPR + ((2 * ds + hh) ^ swz_k<D>(row))) * 16;
+  }
+  // V^T operand of step (db, st), half r: lane (group g16, t4, u4) reads 8 bytes of
+  // row 16 st + 8 (g16 >> 1) + 4 r + t4 at column 32 db + 16 (g16 & 1) + 4 u4. The
+  // swizzle depends on the row only through t4, so one address per db. Bank check:
+  // the 32 lanes of a half-wave read 4 rows x 4 chunks; the XOR by 4*(row & 3)
+  // (d = 128) or 4*((row >> 1) & 1) (d = 64) spreads them over distinct banks.
+  int vaddr[D / 32];
+  {
+    const int g16 = lane >> 4, t4 = (lane & 15) >> 2, u4 = lane & 3;
+    const int row = (g16 >> 1) * 8 + t4;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
+      vaddr[db] = (row * CPR + ((4 * db + 2 * (g16 & 1) + (u4 >> 1)) ^ swz_v<D>(row))) * 16 +
+                  (u4 & 1) * 8;
   }
-  const float c = p.c;
-  // lane-constant LDS byte offsets of the K operand row and the V^T transposed reads
-  const int k_lane = (key_of_row(l32) * G::KPC + hh) * 16;
-  const int g16 = lane >> 4, t4 = (lane & 15) >> 2, u4 = lane & 3;
-  const int v_lane = (((g16 >> 1) * 8 + t4) * G::VPC + (g16 & 1) * 2 + (u4 >> 1)) * 16 + (u4 & 1) * 8;
-
-  constexpr int NQK = (BC / 32) * (D / 16);   // K fragments (S^T MFMA steps) per tile
-  constexpr int NPV = (D / 32) * (BC / 16);   // V fragments (P V MFMA steps) per tile
-  constexpr int SPQ = BC / 2;                 // scores per lane per query block and tile
-  constexpr int NSC = SPQ * QB;               // scores per lane per tile
-  constexpr int SPS = NSC / NQK;              // scores exponentiated per S^T step
-  constexpr int MPS = NSC / NPV;              // scores max-reduced per P V step
-  static_assert(SPS % 2 == 0 && NSC % NQK == 0 && NSC % NPV == 0, "pipeline step split");
-  typedef f32x16_t STile[BC / 32][QB];        // S^T accumulators of one key tile
-  const unsigned char* const ks_base[2] = {reinterpret_cast<const unsigned char*>(ks0) + k_lane,
-                                           reinterpret_cast<const unsigned char*>(ks1) + k_lane};
-  const unsigned char* const vs_base[2] = {reinterpret_cast<const unsigned char*>(vs0) + v_lane,
-                                           reinterpret_cast<const unsigned char*>(vs1) + v_lane};
-  // flattened score index e -> (query block e / SPQ, key block, accumulator register)
-  auto sc = [](const STile& s, int e) -> float { return s[(e % SPQ) / 16][e / SPQ][e % 16]; };
-
-  // LDS reads of MFMA operands: K fragment of S^T step i, and the two transposed V
-  // reads of P V step i (head-dim block db = i / (BC/16), 16-key step st = i % (BC/16))
-  auto k_frag = [&](const unsigned char* kb_, int i) {
-    const int kb = i / (D / 16), ds = i % (D / 16);
-    return *reinterpret_cast<const u32x4_t*>(kb_ + (kb * 32 * G::KPC + 2 * ds) * 16);
+  auto k_frag = [&](const u32x4_t* kst, int i) {
+    const int kb = i % (BC / 32), ds = i / (BC / 32);
+    return *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(kst) +
+                                             kaddr[ds] + kb * 32 * CPR * 16);
   };
-  auto v_frag = [&](const unsigned char* vb_, int i) {
-    const int db = i / (BC / 16), st = i % (BC / 16);
+  auto v_frag = [&](const u32x4_t* vst, int i) {
+    const int db = i % (D / 32), st = i / (D / 32);
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(vst) + vaddr[db];
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(vb_ + ((16 * st + 0) * G::VPC + 4 * db) * 16));
+        (lds_s16x4_t*)(b + (16 * st + 0) * CPR * 16));
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(vb_ + ((16 * st + 4) * G::VPC + 4 * db) * 16));
+        (lds_s16x4_t*)(b + (16 * st + 4) * CPR * 16));
     const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
     return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
   };
+
+  typedef f32x16_t STile[BC / 32];  // S^T accumulators of one key tile
+  // score e of a tile: key block e / 16, accumulator register e % 16
   auto zero = [](STile& s) {
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-  };
-
-  // plain S^T = K Q^T of one tile (prologue only)
-  auto qk_plain = [&](const unsigned char* kb_, STile& s) {
-    zero(s);
-#pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      const int kb = i / (D / 16), ds = i % (D / 16);
-      const u32x4_t kf = k_frag(kb_, i);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][ds], s[kb][qb]);
-    }
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
   };
 
   // -inf on keys past N and, under the causal mask, on keys after the query; only
@@ -256,126 +258,110 @@ fa_fwd_fast_kernel(const Params p) {
     const int k0 = j * BC;
     const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > wq0);
     if (!masked) return;
+    const int qi = wq0 + l32;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qi = wq0 + qb * 32 + l32;
+    for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + key_of_reg(r, hh);
-          if (key >= N || (CAUSAL && key > qi)) s[kb][qb][r] = -__builtin_inff();
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + key_of_reg(r, hh);
+        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -__builtin_inff();
+      }
   };
 
   // m_new = max(m_old, rowmax S); alpha = exp2(m_old - m_new) rescales l and O~. The
   // whole wave skips it when no row needs it (alpha = 1), or, with tau > 0, when no
   // row's max rose by more than tau (log2 units).
-  auto grow_max = [&](int qb, float mxs) {
-    if (__builtin_amdgcn_ballot_w64(mxs > ms[qb] + p.tau) != 0) {
-      const float ms_new = __builtin_fmaxf(ms[qb], mxs);
-      const float alpha = __builtin_amdgcn_exp2f(ms[qb] - ms_new);
-      ms[qb] = ms_new;
-      l_part[qb] *= alpha;
+  auto grow_max = [&](float mxs) {
+    if (__builtin_amdgcn_ballot_w64(mxs > ms + p.tau) != 0) {
+      const float ms_new = __builtin_fmaxf(ms, mxs);
+      const float alpha = __builtin_amdgcn_exp2f(ms - ms_new);
+      ms = ms_new;
+      l_part *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
   };
 
-  // p = exp2(s*c - m*c) for flattened scores [e0, e0+n); consecutive pairs are packed
-  // into the P V operand of their query block: 16-key step (e % SPQ) / 8, word (e % 8) / 2
-  u32x4_t pb[BC / 16][QB];
-  float lsum[QB][2];
-  auto exp_scores = [&](const STile& s, int e0, int n) {
-#pragma unroll
-    for (int e = e0; e < e0 + n; e += 2) {
-      const int qb = e / SPQ;
-      const float msc = ms[qb];
-      // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc(s, e), c, -msc));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc(s, e + 1), c, -msc));
-      lsum[qb][0] += p0;
-      lsum[qb][1] += p1;
-      pb[(e % SPQ) / 8][qb][(e % 8) / 2] = E::pack(p0, p1);
-    }
-  };
+  u32x4_t pb[BC / 16];  // P~ of the current tile, packed as P V operands
 
-  // Block B: S^T of tile j+1 (MFMA) interleaved with the exponentials of tile j (VALU);
-  // K fragments are read two steps ahead
-  auto qk_exp = [&](const unsigned char* kb_, STile& s_next, const STile& s_cur,
+  // Block B: S^T of tile j+1 (MFMA) interleaved with the exponentials of tile j (VALU)
+  // and this wave's copies of the following tiles (VMEM).
+  auto qk_exp = [&](const u32x4_t* k_next, STile& s_next, const STile& s_cur,
                     const Copies& cp) {
     zero(s_next);
-    u32x4_t kf0 = k_frag(kb_, 0), kf1 = k_frag(kb_, 1);
+    const float msc = ms;
+    float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      const u32x4_t kf2 = (i + 2 < NQK) ? k_frag(kb_, i + 2) : kf1;
-      const int kb = i / (D / 16), ds = i % (D / 16);
+      const int kb = i % (BC / 32), ds = i / (BC / 32);
+      s_next[kb] = E::mfma(k_frag(k_next, i), qf[ds], s_next[kb]);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s_next[kb][qb] = E::mfma(kf0, qf[qb][ds], s_next[kb][qb]);
-      exp_scores(s_cur, i * SPS, SPS);
+      for (int e = i * SPS; e < (i + 1) * SPS; e += 2) {
+        // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e / 16][e % 16], c, -msc));
+        const float p1 =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e / 16][(e + 1) % 16], c, -msc));
+        lsum0 += p0;
+        lsum1 += p1;
+        pb[e / 8][(e % 8) / 2] = E::pack(p0, p1);
+      }
       copy_step(cp, i);
-      kf0 = kf1;
-      kf1 = kf2;
-      __builtin_amdgcn_sched_barrier(0);
     }
+    l_part += lsum0 + lsum1;
+    // keep the exponentials in this block (no sinking into the P V block)
+#pragma unroll
+    for (int st = 0; st < BC / 16; ++st) asm volatile("" : "+v"(pb[st]));
+#if FA_SG_ON
+    __builtin_amdgcn_sched_group_barrier(0x100, FA_SG_PREFETCH, 0);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, FA_SG_B_VALU, 0);
+      if (i < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i + FA_SG_PREFETCH < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
   };
 
   // Block C: P V of tile j (MFMA) interleaved with the row max of tile j+1 (VALU)
-  float mxn[QB][2];
-  auto pv_max = [&](const unsigned char* vb_, const STile& s_next) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mxn[qb][0] = mxn[qb][1] = -__builtin_inff();
-    u32x4_t vf0 = v_frag(vb_, 0), vf1 = v_frag(vb_, 1);
+  auto pv_max = [&](const u32x4_t* v_cur, const STile& s_next) {
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      const u32x4_t vf2 = (i + 2 < NPV) ? v_frag(vb_, i + 2) : vf1;
-      const int db = i / (BC / 16), st = i % (BC / 16);
+      const int db = i % (D / 32), st = i / (D / 32);
+      oacc[db] = E::mfma(v_frag(v_cur, i), pb[st], oacc[db]);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = E::mfma(vf0, pb[st][qb], oacc[db][qb]);
-#pragma unroll
-      for (int e = i * MPS; e < (i + 1) * MPS; ++e)
-        mxn[e / SPQ][e & 1] = __builtin_fmaxf(mxn[e / SPQ][e & 1], sc(s_next, e));
-      vf0 = vf1;
-      vf1 = vf2;
-      __builtin_amdgcn_sched_barrier(0);
+      for (int e = i * MPS; e < (i + 1) * MPS; ++e) {
+        if (e & 1) m1 = __builtin_fmaxf(m1, s_next[e / 16][e % 16]);
+        else m0 = __builtin_fmaxf(m0, s_next[e / 16][e % 16]);
+      }
     }
+    float mx = __builtin_fmaxf(m0, m1);
+    asm volatile("" : "+v"(mx));
+#if FA_SG_ON
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * FA_SG_PREFETCH, 1);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, FA_SG_C_VALU, 1);
+      if (i + FA_SG_PREFETCH < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+#endif
+    return mx;
   };
 
   // One key tile j whose masked S^T is in s_cur and whose max is already folded into
   // ms: exponentials and P V of tile j, overlapped with the S^T, mask and max of tile
   // j+1 (from K slot k_next). On a wave's last tile the look-ahead reads a stale but
   // valid K slot and its result is dropped (`next` false: no max update).
-  static_assert(NDMA <= NQK, "copies fit in the S^T pipeline steps");
-  auto tile = [&](const STile& s_cur, STile& s_next, int k_next, int v_cur, int j, bool next,
-                  const Copies& cp) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb][0] = lsum[qb][1] = 0.f;
-    qk_exp(ks_base[k_next], s_next, s_cur, cp);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_part[qb] += lsum[qb][0] + lsum[qb][1];
+  auto tile = [&](const STile& s_cur, STile& s_next, const u32x4_t* k_next,
+                  const u32x4_t* v_cur, int j, bool next, const Copies& cp) {
+    qk_exp(k_next, s_next, s_cur, cp);
     mask(s_next, j + 1);
-    pv_max(vs_base[v_cur], s_next);
-    if (next) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        grow_max(qb, xhalf_max(__builtin_fmaxf(mxn[qb][0], mxn[qb][1])) * c);
-    }
-  };
-
-  // row max of a tile in log2 units (prologue)
-  auto first_max = [&](const STile& s) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][qb][r]);
-      ms[qb] = xhalf_max(mx) * c;  // tile 0 holds key 0, allowed for every row: finite
-    }
+    const float mx = pv_max(v_cur, s_next);
+    if (next) grow_max(xhalf_max(mx) * c);
   };
 
   // ---- main loop ---------------------------------------------------------------------
@@ -383,26 +369,39 @@ fa_fwd_fast_kernel(const Params p) {
   // finished (V_j in vs[j%2]) the S^T of tile j+1 is computed from ks[(j+1)%2], and
   // the copies of K_{j+2} (into ks[j%2]) and V_{j+1} (into vs[(j+1)%2]) are in flight.
   STile sa, sb;
-  issue_k(ks0, 0);
-  issue_v(vs0, 0);
-  if (n_kt > 1) issue_k(ks1, 1);
+  {
+    const Copies c0 = {ks0, vs0, 0, 0};
+    copy_all(c0);
+#pragma unroll
+    for (int ii = 0; ii < G::PER_WAVE; ++ii) copy(kg, ks1, koff[ii], ii, 1);
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (wave_live) {
-    qk_plain(ks_base[0], sa);
+    zero(sa);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int kb = i % (BC / 32), ds = i / (BC / 32);
+      sa[kb] = E::mfma(k_frag(ks0, i), qf[ds], sa[kb]);
+    }
     mask(sa, 0);
-    first_max(sa);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sa[kb][r]);
+    ms = xhalf_max(mx) * c;  // tile 0 holds key 0, allowed for every row: finite
   }
   __syncthreads();  // every wave is done with ks0 before K_2 overwrites it
   for (int j = 0; j < n_kt; j += 2) {
     const Copies ce = {ks0, vs1, j + 2, j + 1};
-    if (wave_live && j < w_kt) tile(sa, sb, 1, 0, j, j + 1 < w_kt, ce);
+    if (wave_live && j < w_kt) tile(sa, sb, ks1, vs0, j, j + 1 < w_kt, ce);
     else copy_all(ce);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 >= n_kt) break;
     const Copies co = {ks1, vs0, j + 3, j + 2};
-    if (wave_live && j + 1 < w_kt) tile(sb, sa, 0, 1, j + 1, j + 2 < w_kt, co);
+    if (wave_live && j + 1 < w_kt) tile(sb, sa, ks0, vs1, j + 1, j + 2 < w_kt, co);
     else copy_all(co);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -411,25 +410,22 @@ fa_fwd_fast_kernel(const Params p) {
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
   if (!wave_live) return;
   const float kLn2 = 0.69314718055994530942f;
+  const float l_tot = xhalf_sum(l_part);
+  const int qi = wq0 + l32;
+  if (qi >= N) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* orow = p.o + head + (size_t)qi * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = xhalf_sum(l_part[qb]);
-    const int qi = wq0 + qb * 32 + l32;
-    if (qi >= N) continue;
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow = p.o + head + (size_t)qi * D;
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dcol = db * 32 + g * 8 + hh * 4;
-        const f32x16_t& a = oacc[db][qb];
-        const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
-        const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
-      }
-    if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  }
+    for (int g = 0; g < 4; ++g) {
+      const int dcol = db * 32 + g * 8 + hh * 4;
+      const f32x16_t& a = oacc[db];
+      const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
+      const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
+    }
+  if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace fa
