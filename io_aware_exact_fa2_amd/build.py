@@ -3,7 +3,8 @@
     python -m io_aware_exact_fa2_amd.build
 
 compiles csrc/fa_fwd.hip into io_aware_exact_fa2_amd/libfa.so. Packed fp32 VALU
-forms are disabled for all device code (-packed-fp32-ops).
+forms are disabled for all device code (-packed-fp32-ops), and MFMA builtins use
+their VGPR-accumulator form.
 """
 from __future__ import annotations
 
@@ -21,6 +22,11 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA builtins accumulate in VGPRs (the wide kernel keeps its output
+    # accumulators in AGPRs through inline assembly, and its S^T tiles, which the
+    # VALU reads, in VGPRs; by default the compiler would put both in AGPRs once a
+    # kernel may use more than 256 registers)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -66,6 +66,25 @@ template <> struct Elt<false> {
   }
 };
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// Word 3 of a raw (stride 0) buffer resource on CDNA: 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+
+// XOR swizzles of the 16-byte chunks of LDS row `row` of a K tile and of a V tile
+// (head dim D, rows of D/8 chunks). Both are permutations of a row's chunks, chosen
+// so the operand reads of the fast kernels are bank-conflict free: 16 lanes reading
+// one logical chunk of 16 different K rows hit 16 different bank quads, and the
+// 4-row x 4-chunk transposed reads of V spread over distinct banks.
+template <int D> __device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

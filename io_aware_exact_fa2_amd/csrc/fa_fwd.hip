@@ -3,6 +3,7 @@
 #include "fa.h"
 #include "fa_fwd_fast.hpp"
 #include "fa_fwd_generic.hpp"
+#include "fa_fwd_wide.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -30,6 +31,19 @@ thread_local int g_last_hip_error = 0;
 #endif
 #ifndef FA_WPE_D64
 #define FA_WPE_D64 2
+#endif
+// The 64-query-per-wave kernel (one wave per SIMD) instead of the 32-query one
+#ifndef FA_WIDE_D128
+#define FA_WIDE_D128 1
+#endif
+#ifndef FA_WIDE_D64
+#define FA_WIDE_D64 0
+#endif
+#ifndef FA_WIDE_RING
+#define FA_WIDE_RING 4    // LDS ring slots per tensor
+#endif
+#ifndef FA_WIDE_BC
+#define FA_WIDE_BC 64
 #endif
 constexpr int kFNW = FA_FAST_NW;
 constexpr int kNW = 4;                    // generic path: waves per workgroup
@@ -86,6 +100,16 @@ hipError_t launch_fast(fa::Params p, hipStream_t stream) {
 }
 
 template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_wide(fa::Params p, hipStream_t stream) {
+  using G = fa::WideGeom<D, FA_WIDE_BC, FA_WIDE_RING>;
+  p.n_qt = (p.N + G::BR - 1) / G::BR;
+  const int grid = p.n_qt * p.BH;
+  auto kern = fa::fa_fwd_wide_kernel<BF16, D, CAUSAL, FA_WIDE_BC, FA_WIDE_RING>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_generic(fa::Params p, hipStream_t stream) {
   p.n_qt = (p.N + kGBR - 1) / kGBR;
   const int grid = p.n_qt * p.BH;
@@ -124,8 +148,13 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   if (!fast) {
     if (d <= 64) e = cz ? launch_generic<BF16, 64, true>(p, s) : launch_generic<BF16, 64, false>(p, s);
     else e = cz ? launch_generic<BF16, 128, true>(p, s) : launch_generic<BF16, 128, false>(p, s);
-  } else if (d == 128) e = cz ? launch_fast<BF16, 128, true>(p, s) : launch_fast<BF16, 128, false>(p, s);
-  else e = cz ? launch_fast<BF16, 64, true>(p, s) : launch_fast<BF16, 64, false>(p, s);
+  } else if (d == 128) {
+    if (FA_WIDE_D128) e = cz ? launch_wide<BF16, 128, true>(p, s) : launch_wide<BF16, 128, false>(p, s);
+    else e = cz ? launch_fast<BF16, 128, true>(p, s) : launch_fast<BF16, 128, false>(p, s);
+  } else {
+    if (FA_WIDE_D64) e = cz ? launch_wide<BF16, 64, true>(p, s) : launch_wide<BF16, 64, false>(p, s);
+    else e = cz ? launch_fast<BF16, 64, true>(p, s) : launch_fast<BF16, 64, false>(p, s);
+  }
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return FA_ERR_HIP;

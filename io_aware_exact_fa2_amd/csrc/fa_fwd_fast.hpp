@@ -69,22 +69,6 @@
 
 namespace fa {
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// Word 3 of a raw (stride 0) buffer resource on CDNA: 32-bit data format.
-constexpr int kBufferWord3 = 0x00020000;
-
-// XOR swizzles of the 16-byte chunks of LDS row `row` (K rows, V rows). Both are
-// permutations of a row's chunks; see the bank analysis where they are used.
-template <int D> __device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D> __device__ __forceinline__ int swz_v(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
 template <int D_, int NW_, int BC_>
 struct FastGeom {
   static constexpr int D = D_;

@@ -1,0 +1,576 @@
+// fa_fwd_wide.hpp — FA2-order attention forward for gfx950 (MI355X): one wave per
+// SIMD, 64 queries per wave, for head dims 64 and 128.
+//
+// Algorithm ([P1] currybab.bearblog.dev, "Triton으로 FlashAttention 구현하기 전에 -
+// FA1, 2 forward pass", section "FlashAttention 2 forward pass 알고리즘 분석"): the
+// query row block is the outer loop (one workgroup per query block, head and batch),
+// key/value blocks stream through LDS in the inner loop, each row keeps its running
+// max and sum on chip, rescales the unnormalised output by alpha = exp(m_old - m_new)
+// only, and divides once at the end. Waves own disjoint query rows (split-Q), so no
+// cross-wave merge exists.
+//
+// Why a second fast kernel: with 32 queries per wave, every K or V operand read from
+// LDS feeds exactly one 32x32x16 MFMA, and the LDS read bandwidth of a CU then equals
+// its MFMA rate, so LDS and the matrix cores bound each other. Here each wave owns
+// two 32-query column blocks and every operand read from LDS feeds two MFMAs, which
+// halves the LDS traffic per flop. The price is registers: the two output
+// accumulators alone take 128 of them at d = 128, so a wave gets the whole register
+// file of its SIMD (one wave per SIMD, four per workgroup) and hides latency by
+// software pipelining only.
+//
+// gfx950 mapping:
+//   * K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register
+//     staging) into a ring of R slots each. Iteration j issues K_{j+R} and V_{j+R-1};
+//     every copy has R - 1 iterations to land, and the end-of-iteration wait leaves
+//     the newest R - 2 iterations of copies in flight (vmcnt counts this wave's copies
+//     in issue order). One barrier per iteration makes the other waves' copies
+//     visible and frees the slots for the next copies.
+//   * K runs one tile ahead of V: while tile j is finished, the S^T MFMAs of tile j+1
+//     are interleaved with the first half of the exponentials of tile j, and the P V
+//     MFMAs of tile j with the second half and then with the row max of tile j+1.
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}; each lane owns
+//     one query column per block, so the running max/sum and the alpha rescale are
+//     in-lane, and the S^T accumulator rounded to 16 bits is the B operand of P V
+//     (key rows enter with bits 2 and 3 of the row index swapped).
+//   * LDS layout, XOR swizzles, transposed V reads (ds_read_b64_tr_b16), exp2 with the
+//     log2(e) factor folded into the scale, the lazy rescale threshold tau and the
+//     causal tile skipping are those of the 32-query kernel.
+#pragma once
+
+#include "fa_common.hpp"
+
+#ifndef FA_W_PF
+#define FA_W_PF 2         // MFMA steps an LDS operand read runs ahead
+#endif
+#ifndef FA_W_EXPB_ST
+#define FA_W_EXPB_ST 3    // 16-key P steps (of BC/16) exponentiated in the S^T block
+#endif
+
+namespace fa {
+
+template <int D_, int BC_, int R_>
+struct WideGeom {
+  static constexpr int D = D_;
+  static constexpr int BC = BC_;
+  static constexpr int R = R_;                   // ring slots per tensor
+  static constexpr int NW = 4;                   // waves per workgroup, one per SIMD
+  static constexpr int QB = 2;                   // 32-query blocks per wave
+  static constexpr int BR = NW * QB * 32;        // queries per workgroup
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int CHUNKS = BC * CPR;        // chunks per K (or V) tile
+  static constexpr int INSTR = CHUNKS / 64;      // 1 KB wave copies per tile and tensor
+  static constexpr int PER_WAVE = INSTR / NW;    // copies per wave per tile and tensor
+  static constexpr int NQK = (BC / 32) * (D / 16);  // S^T steps per tile (2 MFMAs each)
+  static constexpr int NPV = (D / 32) * (BC / 16);  // P V steps per tile (2 MFMAs each)
+  static constexpr int NST = BC / 16;            // 16-key P operands per query block
+  static_assert(D == 64 || D == 128, "fast path head dims");
+  static_assert(BC % 32 == 0 && CHUNKS % 64 == 0, "whole MFMA blocks and wave copies");
+  static_assert(INSTR % NW == 0 && PER_WAVE >= 1, "every wave issues the same copies");
+  static_assert(2 * PER_WAVE <= NQK, "copies fit in the S^T pipeline steps");
+  static_assert(R >= 2 && R % 2 == 0, "ring of an even number of slots");
+  static_assert(2 * PER_WAVE * (R - 1) <= 63, "outstanding copies fit the vmcnt field");
+};
+
+// O~ += A B with the accumulator held in AGPRs (the S^T accumulators stay in VGPRs,
+// where the VALU reads them). Written out because the compiler picks one register
+// file for all MFMA accumulators of a kernel.
+template <bool BF16>
+__device__ __forceinline__ void mfma_acc_agpr(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+  if (BF16)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Raw buffer resource over `bytes` bytes at address a (stride 0, 32-bit format): reads
+// past the end return zeros.
+__device__ __forceinline__ u32x4_t buffer_rsrc(uint64_t a, uint32_t bytes) {
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
+}
+
+// The copies and the Q loads are issued as inline assembly, so the compiler's memory
+// counter model does not see them and adds no waits of its own: the kernel orders
+// them with explicit vmcnt waits and its ring barrier. One 16-byte-per-lane HBM -> LDS
+// copy: lane l's 16 bytes at byte offset voff of the buffer land at LDS address
+// lds + lds_off + 16 l (M0 holds the wave's LDS base); bytes past the buffer's size
+// read as 0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4_t rsrc, uint32_t voff, uint32_t lds,
+                                           int lds_off /* a constant after unrolling */) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds), "n"(lds_off) : "m0", "scc");
+}
+#pragma clang diagnostic pop
+// 16-byte global load; the result may only be read after an explicit vmcnt wait
+// that covers it.
+__device__ __forceinline__ u32x4_t global_load16(const uint16_t* p) {
+  u32x4_t x;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p));
+  return x;
+}
+
+// x = (c <= t) ? x : -inf, with c a constant after unrolling. Compare and select
+// stay one pair, so no lane masks pile up in scalar registers across a tile.
+__device__ __forceinline__ float keep_if_le(float x, int c, int t) {
+  // v_cndmask reads VCC, so -inf comes from a register (one constant-bus operand)
+  asm("v_cmp_le_i32 vcc, %2, %1\n\tv_cndmask_b32 %0, %3, %0, vcc"
+      : "+v"(x) : "v"(t), "n"(c), "v"(-__builtin_inff()) : "vcc");
+  return x;
+}
+
+template <bool BF16, int D, bool CAUSAL, int BC, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_fwd_wide_kernel(const Params p) {
+  using G = WideGeom<D, BC, R>;
+  using E = Elt<BF16>;
+  constexpr int NW = G::NW, CPR = G::CPR, NQK = G::NQK, NPV = G::NPV, NST = G::NST;
+  constexpr int CHUNKS = G::CHUNKS, PW = G::PER_WAVE, NDMA = 2 * PW;
+  // Work split of one tile's VALU work over the 2 * (NQK + NPV) MFMAs. A lane holds
+  // NSC scores per tile (both query blocks). The exponentials of the first
+  // FA_W_EXPB_ST 16-key P steps are spread over the S^T block, the rest over the P V
+  // steps before the first one that consumes them, and the row max of the next tile
+  // over all P V steps. Counts are in score pairs (one packed P word each).
+  constexpr int NSC = 2 * (BC / 2);
+  constexpr int EXPB_ST = FA_W_EXPB_ST < NST ? FA_W_EXPB_ST : NST;
+  constexpr int PAIRS_B = EXPB_ST * 8;                  // pairs exponentiated in block B
+  constexpr int PAIRS_C = NSC / 2 - PAIRS_B;            // pairs exponentiated in block C
+  // P V steps that carry them: all before the first step consuming P step EXPB_ST,
+  // less one, so a whole MFMA step separates the last VALU write of a P operand from
+  // the (inline assembly) MFMA that reads it
+  constexpr int C_EXP_STEPS = EXPB_ST * (D / 32) - 1;
+  constexpr int PAIRS_M = NSC / 2;                      // max pairs, over all P V steps
+  static_assert(EXPB_ST >= 1 && (PAIRS_C == 0 || C_EXP_STEPS >= 1), "pipeline step split");
+  // K ring and V ring; slot u of a ring holds one tile at offset u * CHUNKS
+  __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
+  __shared__ __attribute__((aligned(1024))) u32x4_t vbuf[R * CHUNKS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int N = p.N;
+
+  int bh, qt;
+  decode_tile<CAUSAL>(p, blockIdx.x, bh, qt);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* __restrict__ qg = p.q + head;
+  const uint16_t* __restrict__ kg = p.k + head;
+  const uint16_t* __restrict__ vg = p.v + head;
+
+  const int q0 = qt * G::BR;
+  const int wq0 = q0 + wid * 64;
+  const int q_end = min(q0 + G::BR, N);
+  const int n_kt = CAUSAL ? (q_end + BC - 1) / BC : (N + BC - 1) / BC;
+  const bool wave_live = wq0 < N;
+  const int w_last_q = min(wq0 + 64, N) - 1;
+  const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
+
+  // ---- HBM -> LDS copies ---------------------------------------------------------
+  // Lane `lane` of copy instruction i writes LDS chunk 64 i + lane = (row, physical
+  // chunk) of a tile; it fetches the logical chunk that the swizzle puts there.
+  // Copy ii covers rows 64 NW ii / CPR further down than copy 0, a multiple of 16 rows,
+  // and both swizzles depend on the row only modulo 16: the byte offsets of copy ii
+  // are those of copy 0 plus II_BYTES * ii.
+  constexpr uint32_t II_BYTES = NW * 64 * 16;
+  static_assert((NW * 64 / CPR) % 16 == 0, "copies are whole 16-row groups");
+  uint32_t koff, voff;
+  {
+    const int f = wid * 64 + lane, row = f / CPR, ph = f % CPR;
+    koff = (uint32_t)(row * D + (ph ^ swz_k<D>(row)) * 8) * 2u;
+    voff = (uint32_t)(row * D + (ph ^ swz_v<D>(row)) * 8) * 2u;
+  }
+  // One copy of tile j. The buffer resource spans the tile's rows below N, so chunks
+  // of rows past N read as zeros (their scores are masked to -inf). Tiles past the
+  // last are clamped to it: such a copy lands in a slot no later tile reads.
+  // The buffer of tile j spans its rows below N: the range check zero-fills the rest.
+  auto tile_rsrc = [&](const uint16_t* src, int j) {
+    const int k0 = min(j, n_kt - 1) * BC;
+    return buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)k0 * D),
+                       (uint32_t)(min(N - k0, BC) * D * 2));
+  };
+  // LDS byte address of this wave's first chunk in slot 0 of each ring; the slot
+  // and copy offsets are immediates
+  const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(kbuf + wid * 64));
+  const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(vbuf + wid * 64));
+  struct Copies {
+    int k_slot, v_slot;
+    int jk, jv;
+  };
+  // copy step i of a tile: K copies first, then V copies
+  auto copy_step = [&](const Copies& cp, int i) {
+    if (i < PW)
+      lds_copy16(tile_rsrc(kg, cp.jk), koff + II_BYTES * i, k_lds,
+                 cp.k_slot * CHUNKS * 16 + i * NW * 1024);
+    else if (i < NDMA)
+      lds_copy16(tile_rsrc(vg, cp.jv), voff + II_BYTES * (i - PW), v_lds,
+                 cp.v_slot * CHUNKS * 16 + (i - PW) * NW * 1024);
+  };
+  auto copy_all = [&](const Copies& cp) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) copy_step(cp, i);
+  };
+
+  // ---- Q fragments (B operands of S^T = K Q^T), in registers for the whole loop -----
+  // Issued before any copy, so the first wait for K_0 also covers them. Rows past N
+  // load row N-1: their columns are never stored.
+  u32x4_t qf[2][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = min(wq0 + 32 * qb + l32, N - 1);
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds)
+      qf[qb][ds] = global_load16(qg + (size_t)qi * D + ds * 16 + hh * 8);
+  }
+
+  // ---- prologue copies: K_0, then (K_t, V_{t-1}) for t = 1 .. R-1 ---------------------
+  // the same (K, V) pairing as the main loop, so one vmcnt formula serves both
+#pragma unroll
+  for (int i = 0; i < PW; ++i) copy_step(Copies{0, 0, 0, 0}, i);
+#pragma unroll
+  for (int t = 1; t < R; ++t) copy_all(Copies{t, t - 1, t, t - 1});
+
+  // ---- running state ---------------------------------------------------------------
+  f32x16_t oacc[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
+  float ms[2] = {0.f, 0.f};
+  float ls[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // per-lane running sums, two chains each
+  const float c = p.c;
+
+  // ---- per-lane LDS read addresses (see the 32-query kernel for the bank analysis) --
+  // Absolute LDS byte addresses of slot 0, pinned in registers, so that the slot and
+  // step offsets (all below 64 KB) become the immediate offsets of the reads even
+  // when the ring itself lies above 64 KB.
+  // K: the row pitch is a multiple of 128 bytes and the swizzle acts on chunk bits
+  // only, so the address of step ds is that of step 0 with (2 ds) << 4 XORed in
+  // (the logical chunk 2 ds + hh enters the XOR linearly).
+  uint32_t kaddr0;
+  {
+    const int row = key_of_row(l32);
+    kaddr0 = (uint32_t)(uintptr_t)kbuf + (row * CPR + (hh ^ swz_k<D>(row))) * 16;
+    asm volatile("" : "+v"(kaddr0));
+  }
+  uint32_t vaddr[D / 32];
+  {
+    const int g16 = lane >> 4, t4 = (lane & 15) >> 2, u4 = lane & 3;
+    const int row = (g16 >> 1) * 8 + t4;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      vaddr[db] = (uint32_t)(uintptr_t)vbuf +
+                  (row * CPR + ((4 * db + 2 * (g16 & 1) + (u4 >> 1)) ^ swz_v<D>(row))) * 16 +
+                  (u4 & 1) * 8;
+      asm volatile("" : "+v"(vaddr[db]));
+    }
+  }
+  typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+  auto k_frag = [&](int slot, int i) {
+    const int kb = i % (BC / 32), ds = i / (BC / 32);
+    return *(lds_u32x4_t*)(uintptr_t)((kaddr0 ^ (uint32_t)(ds << 5)) + slot * CHUNKS * 16 +
+                                      kb * 32 * CPR * 16);
+  };
+  auto v_frag = [&](int slot, int i) {
+    const int db = i % (D / 32), st = i / (D / 32);
+    const uint32_t b = vaddr[db] + slot * CHUNKS * 16;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(uintptr_t)(b + (16 * st + 0) * CPR * 16));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4_t*)(uintptr_t)(b + (16 * st + 4) * CPR * 16));
+    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+    return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+  };
+
+  // S^T accumulators of one key tile: [key block][query block]; score e of a lane's
+  // query column (0 <= e < BC/2) is register e % 16 of key block e / 16
+  typedef f32x16_t STile[BC / 32][2];
+  auto zero = [](STile& s) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+  };
+  // S^T of a whole tile from K slot kst, without interleaved work
+  auto qk_plain = [&](int kst, STile& s) {
+    zero(s);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int kb = i % (BC / 32), ds = i / (BC / 32);
+      const u32x4_t kf = k_frag(kst, i);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][ds], s[kb][qb]);
+    }
+  };
+
+  // -inf on keys past N and, under the causal mask, on keys after the query; only
+  // tiles that reach past N or cross the diagonal need it
+  auto mask = [&](STile& s, int j) {
+    const int k0 = j * BC;
+    const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > wq0);
+    if (!masked) return;
+    // With key = k0 + 8 hh + c (c = 32 kb + key_of_reg(r, 0), a constant per register),
+    // a score is kept iff c <= t, where t is the last allowed key of the lane's query
+    // (below N, and not after the query under the causal mask) minus k0 + 8 hh: one
+    // compare against a per-lane value per register.
+    const int base = k0 + 8 * hh;
+    // the compares are inline assembly, which the compiler's hazard tracking does
+    // not see: wait out the S^T MFMAs first (an 8-pass XDL result needs about a
+    // dozen wait states before a VALU access), taking the tile as operands so the
+    // compares stay behind the padding
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]));
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        if (kb + qb > 0) asm volatile("" : "+v"(s[kb][qb]));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int last = CAUSAL ? min(N - 1, wq0 + 32 * qb + l32) : N - 1;
+      const int t = last - base;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kb][qb][r] = keep_if_le(s[kb][qb][r], kb * 32 + key_of_reg(r, 0), t);
+    }
+  };
+
+  // m_new = max(m_old, rowmax S); alpha = exp2(m_old - m_new) rescales l and O~ of one
+  // query block. The wave skips it when no row's max rose by more than tau (log2 units).
+  // The compiler does not know that the P V MFMAs (inline assembly) write O~, so it
+  // inserts no wait states before VALU accesses of O~: this pads them (an 8-pass
+  // XDL result needs about a dozen) and, by taking the accumulators as operands,
+  // keeps every such access after the padding.
+  auto drain_o = [&](int qb) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[0][qb]));
+#pragma unroll
+    for (int db = 1; db < D / 32; ++db) asm volatile("" : "+a"(oacc[db][qb]));
+  };
+  auto grow_max = [&](int qb, float mxs) {
+    if (__builtin_amdgcn_ballot_w64(mxs > ms[qb] + p.tau) != 0) {
+      const float ms_new = __builtin_fmaxf(ms[qb], mxs);
+      const float alpha = __builtin_amdgcn_exp2f(ms[qb] - ms_new);
+      ms[qb] = ms_new;
+      ls[qb][0] *= alpha;
+      ls[qb][1] *= alpha;
+      drain_o(qb);
+      // one 16-register block at a time (it passes through VGPRs), so the rescale
+      // needs few registers while both S^T tiles are live
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
+        asm volatile("" : "+a"(oacc[db][qb]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  u32x4_t pb[2][NST];  // P~ of the current tile, packed as P V operands
+
+  // exponentials of flat score indices [t0, t1) of the current tile: index t is score
+  // 8 (t / 16) + t % 8 of query block (t / 8) % 2, i.e. the P operands are produced in
+  // the order the P V steps consume them (16-key step major, query block minor). The
+  // results are pinned, so they are computed in the pipeline step that calls this.
+  auto exps = [&](const STile& s, int t0, int t1) {
+#pragma unroll
+    for (int t = t0; t < t1; t += 2) {
+      const int qb = (t / 8) % 2, e = 8 * (t / 16) + t % 8;
+      // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
+      const float p0 =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][qb][e % 16], c, -ms[qb]));
+      const float p1 =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][qb][(e + 1) % 16], c, -ms[qb]));
+      ls[qb][0] += p0;
+      ls[qb][1] += p1;
+      uint32_t w = E::pack(p0, p1);
+      asm volatile("" : "+v"(w));
+      pb[qb][e / 8][(e % 8) / 2] = w;
+    }
+    asm volatile("" : "+v"(ls[0][0]), "+v"(ls[0][1]), "+v"(ls[1][0]), "+v"(ls[1][1]));
+  };
+
+  // The two blocks below are software pipelines of MFMA steps. Each step is fenced
+  // with sched_barrier, so its MFMAs, its share of the VALU work and the LDS operand
+  // read for FA_W_PF steps later stay together: the matrix cores and the VALU then
+  // work side by side from one wave, which is all the latency hiding a wave that is
+  // alone on its SIMD has.
+
+  // Block B: S^T of tile j+1 (MFMA) interleaved with the first half of the
+  // exponentials of tile j (VALU) and this wave's copies of later tiles, one every
+  // NQK / NDMA steps so the four waves do not queue their copies all at once. A copy
+  // is inline assembly, which orders the LDS reads around it: it comes after its
+  // step's read.
+  static_assert(NQK % NDMA == 0, "copies spread evenly over the S^T steps");
+  auto block_b = [&](int k_next, STile& s_next, const STile& s_cur, const Copies& cp,
+                     int v_cur, u32x4_t* vpre) {
+    zero(s_next);
+    u32x4_t kf[NQK];
+#pragma unroll
+    for (int i = 0; i < FA_W_PF; ++i) kf[i] = k_frag(k_next, i);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      if (i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(k_next, i + FA_W_PF);
+      const int kb = i % (BC / 32), ds = i / (BC / 32);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s_next[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_next[kb][qb]);
+      exps(s_cur, 2 * (i * PAIRS_B / NQK), 2 * ((i + 1) * PAIRS_B / NQK));
+      if (i % (NQK / NDMA) == 0) copy_step(cp, i / (NQK / NDMA));
+      // the first operand reads of the P V block run ahead across the block boundary
+      if (i >= NQK - FA_W_PF) vpre[i - (NQK - FA_W_PF)] = v_frag(v_cur, i - (NQK - FA_W_PF));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Block C: P V of tile j (MFMA), interleaved first with the second half of the
+  // exponentials of tile j, then with the row max of tile j+1 (VALU). Returns the
+  // per-lane maxima of the two query blocks of tile j+1.
+  auto block_c = [&](int v_cur, const STile& s_cur, const STile& s_next, const u32x4_t* vpre,
+                     float& mx0, float& mx1) {
+    float m[2][2] = {{-__builtin_inff(), -__builtin_inff()},
+                     {-__builtin_inff(), -__builtin_inff()}};
+    u32x4_t vf[NPV];
+#pragma unroll
+    for (int i = 0; i < FA_W_PF; ++i) vf[i] = vpre[i];
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      // The compiler does not know the MFMAs below read their sources over several
+      // cycles (they are inline assembly): keep the previous step's sources live
+      // until this step, so no VALU result is written into them right behind the MFMA.
+      if (i > 0) asm volatile("" ::"v"(vf[i - 1]), "v"(pb[0][(i - 1) / (D / 32)]),
+                              "v"(pb[1][(i - 1) / (D / 32)]));
+      if (i + FA_W_PF < NPV) vf[i + FA_W_PF] = v_frag(v_cur, i + FA_W_PF);
+      const int db = i % (D / 32), st = i / (D / 32);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) mfma_acc_agpr<BF16>(oacc[db][qb], vf[i], pb[qb][st]);
+      if (i < C_EXP_STEPS)
+        exps(s_cur, 2 * PAIRS_B + 2 * (i * PAIRS_C / C_EXP_STEPS),
+             2 * PAIRS_B + 2 * ((i + 1) * PAIRS_C / C_EXP_STEPS));
+      {
+#pragma unroll
+        for (int t = 2 * (i * PAIRS_M / NPV); t < 2 * ((i + 1) * PAIRS_M / NPV); t += 2) {
+          const int qb = t / (BC / 2), e = t % (BC / 2);
+          m[qb][0] = __builtin_fmaxf(m[qb][0], s_next[e / 16][qb][e % 16]);
+          m[qb][1] = __builtin_fmaxf(m[qb][1], s_next[e / 16][qb][(e + 1) % 16]);
+        }
+        asm volatile("" : "+v"(m[0][0]), "+v"(m[0][1]), "+v"(m[1][0]), "+v"(m[1][1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mx0 = __builtin_fmaxf(m[0][0], m[0][1]);
+    mx1 = __builtin_fmaxf(m[1][0], m[1][1]);
+  };
+
+  // One key tile j whose masked S^T is in s_cur and whose max is already folded into
+  // ms: exponentials and P V of tile j, overlapped with the S^T, mask and max of tile
+  // j+1 (from K slot k_next). On a wave's last tile the look-ahead reads a slot that
+  // holds a stale or clamped tile, and its result is dropped (`next` false).
+  auto tile = [&](const STile& s_cur, STile& s_next, int k_next, int v_cur, int j, bool next,
+                  const Copies& cp) {
+    u32x4_t vpre[FA_W_PF];
+    block_b(k_next, s_next, s_cur, cp, v_cur, vpre);
+    mask(s_next, j + 1);
+    float mx0, mx1;
+    block_c(v_cur, s_cur, s_next, vpre, mx0, mx1);
+    if (next) {
+      grow_max(0, xhalf_max(mx0) * c);
+      grow_max(1, xhalf_max(mx1) * c);
+    }
+  };
+
+  // After this wave's copies for tiles up to (K_{j+2}, V_{j+1}) have landed, the newest
+  // R - 2 iterations of copies may still be in flight.
+  auto wait_ring = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * (R - 2)) : "memory");
+  };
+  // Workgroup barrier for the ring. This wave's LDS reads are complete before it
+  // (lgkmcnt), so after it another wave may overwrite the slots they read; copies
+  // are ordered by the explicit vmcnt waits. The memory clobber keeps LDS accesses
+  // and copies on their side of it. (A full __syncthreads fence would also wait for
+  // the copies still in flight, which the ring is there to avoid.)
+  auto ring_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // ---- S^T of tile 0 and the initial reference max ------------------------------------
+  STile sa, sb;
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * (R - 1)) : "memory");  // Q and K_0
+  // Q has landed: sign flip for a negative scale, then Q lives in AGPRs (MFMA source
+  // operands may come from either register file), leaving the VGPRs to the S^T
+  // tiles and the VALU work
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      asm volatile("" : "+v"(qf[qb][ds]));
+      qf[qb][ds] ^= p.qsign;
+      asm volatile("" : "+a"(qf[qb][ds]));
+    }
+  ring_barrier();
+  if (wave_live) {
+    qk_plain(0, sa);
+    mask(sa, 0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sa[kb][qb][r]);
+      // tile 0 holds key 0, allowed for every row: finite
+      ms[qb] = xhalf_max(mx) * c;
+    }
+  }
+  wait_ring();  // K_1 and V_0
+  ring_barrier();  // and every wave is done with slot 0 of K before K_R overwrites it
+
+  // ---- main loop: slots of tile j are j % R (K and V), unrolled over the ring --------
+  for (int j0 = 0; j0 < n_kt; j0 += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int j = j0 + u;
+      if (j >= n_kt) break;
+      const Copies cp = {u, (u + R - 1) % R, j + R, j + R - 1};
+      STile& s_cur = (u % 2 == 0) ? sa : sb;
+      STile& s_nxt = (u % 2 == 0) ? sb : sa;
+      if (wave_live && j < w_kt)
+        tile(s_cur, s_nxt, (u + 1) % R, u, j, j + 1 < w_kt, cp);
+      else
+        copy_all(cp);
+      wait_ring();
+      ring_barrier();
+    }
+  }
+
+  // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
+  if (!wave_live) return;
+  const float kLn2 = 0.69314718055994530942f;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    drain_o(qb);
+    const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
+    const int qi = wq0 + 32 * qb + l32;
+    if (qi < N) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = p.o + head + (size_t)qi * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dcol = db * 32 + g * 8 + hh * 4;
+          const f32x16_t& a = oacc[db][qb];
+          const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
+          const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
+        }
+      if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+  }
+}
+
+}  // namespace fa
