@@ -139,7 +139,8 @@ fa_fwd_wide_kernel(const Params p) {
   // less one, so a whole MFMA step separates the last VALU write of a P operand from
   // the (inline assembly) MFMA that reads it
   constexpr int C_EXP_STEPS = EXPB_ST * (D / 32) - 1;
-  constexpr int PAIRS_M = NSC / 2;                      // max pairs, over all P V steps
+  constexpr int PAIRS_M = NSC / 2;                      // max pairs, over the first M_STEPS
+  constexpr int M_STEPS = NPV / 2;                      // P V steps that carry the max
   static_assert(EXPB_ST >= 1 && (PAIRS_C == 0 || C_EXP_STEPS >= 1), "pipeline step split");
   // K ring and V ring; slot u of a ring holds one tile at offset u * CHUNKS
   __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
@@ -352,8 +353,8 @@ fa_fwd_wide_kernel(const Params p) {
 #pragma unroll
     for (int db = 1; db < D / 32; ++db) asm volatile("" : "+a"(oacc[db][qb]));
   };
-  auto grow_max = [&](int qb, float mxs) {
-    if (__builtin_amdgcn_ballot_w64(mxs > ms[qb] + p.tau) != 0) {
+  auto grow_max = [&](int qb, float mxs, uint64_t need) {
+    if (need != 0) {
       const float ms_new = __builtin_fmaxf(ms[qb], mxs);
       const float alpha = __builtin_amdgcn_exp2f(ms[qb] - ms_new);
       ms[qb] = ms_new;
@@ -429,11 +430,13 @@ fa_fwd_wide_kernel(const Params p) {
     }
   };
 
-  // Block C: P V of tile j (MFMA), interleaved first with the second half of the
-  // exponentials of tile j, then with the row max of tile j+1 (VALU). Returns the
-  // per-lane maxima of the two query blocks of tile j+1.
+  // Block C: P V of tile j (MFMA), interleaved with the rest of the exponentials of
+  // tile j and, in its first half, the row max of tile j+1 (VALU). At the middle step
+  // the two wave halves exchange their maxima and the wave votes on the rescale, so the
+  // vote has long completed when the tile ends. Returns the row maxima of the two
+  // query blocks of tile j+1 (log2 units) and the votes.
   auto block_c = [&](int v_cur, const STile& s_cur, const STile& s_next, const u32x4_t* vpre,
-                     float& mx0, float& mx1) {
+                     float& mx0, float& mx1, uint64_t& need0, uint64_t& need1) {
     float m[2][2] = {{-__builtin_inff(), -__builtin_inff()},
                      {-__builtin_inff(), -__builtin_inff()}};
     u32x4_t vf[NPV];
@@ -453,19 +456,24 @@ fa_fwd_wide_kernel(const Params p) {
       if (i < C_EXP_STEPS)
         exps(s_cur, 2 * PAIRS_B + 2 * (i * PAIRS_C / C_EXP_STEPS),
              2 * PAIRS_B + 2 * ((i + 1) * PAIRS_C / C_EXP_STEPS));
-      {
+      if (i < M_STEPS) {
 #pragma unroll
-        for (int t = 2 * (i * PAIRS_M / NPV); t < 2 * ((i + 1) * PAIRS_M / NPV); t += 2) {
+        for (int t = 2 * (i * PAIRS_M / M_STEPS); t < 2 * ((i + 1) * PAIRS_M / M_STEPS); t += 2) {
           const int qb = t / (BC / 2), e = t % (BC / 2);
           m[qb][0] = __builtin_fmaxf(m[qb][0], s_next[e / 16][qb][e % 16]);
           m[qb][1] = __builtin_fmaxf(m[qb][1], s_next[e / 16][qb][(e + 1) % 16]);
         }
         asm volatile("" : "+v"(m[0][0]), "+v"(m[0][1]), "+v"(m[1][0]), "+v"(m[1][1]));
       }
+      if (i == M_STEPS) {
+        mx0 = xhalf_max(__builtin_fmaxf(m[0][0], m[0][1])) * c;
+        mx1 = xhalf_max(__builtin_fmaxf(m[1][0], m[1][1])) * c;
+        need0 = __builtin_amdgcn_ballot_w64(mx0 > ms[0] + p.tau);
+        need1 = __builtin_amdgcn_ballot_w64(mx1 > ms[1] + p.tau);
+        asm volatile("" : "+v"(mx0), "+v"(mx1), "+s"(need0), "+s"(need1));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx0 = __builtin_fmaxf(m[0][0], m[0][1]);
-    mx1 = __builtin_fmaxf(m[1][0], m[1][1]);
   };
 
   // One key tile j whose masked S^T is in s_cur and whose max is already folded into
@@ -478,10 +486,11 @@ fa_fwd_wide_kernel(const Params p) {
     block_b(k_next, s_next, s_cur, cp, v_cur, vpre);
     mask(s_next, j + 1);
     float mx0, mx1;
-    block_c(v_cur, s_cur, s_next, vpre, mx0, mx1);
+    uint64_t need0, need1;
+    block_c(v_cur, s_cur, s_next, vpre, mx0, mx1, need0, need1);
     if (next) {
-      grow_max(0, xhalf_max(mx0) * c);
-      grow_max(1, xhalf_max(mx1) * c);
+      grow_max(0, mx0, need0);
+      grow_max(1, mx1, need1);
     }
   };
 
