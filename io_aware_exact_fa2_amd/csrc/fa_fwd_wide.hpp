@@ -42,9 +42,13 @@
 #ifndef FA_W_PF
 #define FA_W_PF 2         // MFMA steps an LDS operand read runs ahead
 #endif
-#ifndef FA_W_EXPB_ST
-#define FA_W_EXPB_ST 3    // 16-key P steps (of BC/16) exponentiated in the S^T block
+#ifndef FA_W_PAIRS_B128
+#define FA_W_PAIRS_B128 19  // score pairs (of 32) exponentiated in the S^T block, d = 128
 #endif
+#ifndef FA_W_PAIRS_B64
+#define FA_W_PAIRS_B64 18   // the same for d = 64
+#endif
+#define FA_W_PAIRS_B(D) ((D) == 128 ? FA_W_PAIRS_B128 : FA_W_PAIRS_B64)
 
 namespace fa {
 
@@ -70,6 +74,23 @@ struct WideGeom {
   static_assert(R >= 2 && R % 2 == 0, "ring of an even number of slots");
   static_assert(2 * PER_WAVE * (R - 1) <= 63, "outstanding copies fit the vmcnt field");
 };
+
+// Checks the softmax schedule of the P V block: with the units of pairs ub/3 .. npair-1
+// spread evenly over `ces` slots, the last unit of every pair lands at least one slot
+// before the first MFMA that reads its P step (pairs npair/nst per step, steps of `db`
+// slot pairs).
+constexpr bool fa_wide_exp_deadlines(int npair, int nst, int db, int ub, int ces) {
+  const int uc = 3 * npair - ub;
+  if (uc == 0) return true;
+  if (ces <= 0 || ub % 3 != 0) return false;
+  for (int v = ub / 3; v < npair; ++v) {
+    const int rel = 3 * v + 2 - ub;
+    int slot = 0;
+    while ((slot + 1) * uc / ces <= rel) ++slot;  // slot s holds units [s uc/ces, (s+1) uc/ces)
+    if (slot > 2 * (v / (npair / nst)) * db - 2) return false;
+  }
+  return true;
+}
 
 // O~ += A B with the accumulator held in AGPRs (the S^T accumulators stay in VGPRs,
 // where the VALU reads them). Written out because the compiler picks one register
@@ -126,22 +147,32 @@ fa_fwd_wide_kernel(const Params p) {
   using E = Elt<BF16>;
   constexpr int NW = G::NW, CPR = G::CPR, NQK = G::NQK, NPV = G::NPV, NST = G::NST;
   constexpr int CHUNKS = G::CHUNKS, PW = G::PER_WAVE, NDMA = 2 * PW;
-  // Work split of one tile's VALU work over the 2 * (NQK + NPV) MFMAs. A lane holds
-  // NSC scores per tile (both query blocks). The exponentials of the first
-  // FA_W_EXPB_ST 16-key P steps are spread over the S^T block, the rest over the P V
-  // steps before the first one that consumes them, and the row max of the next tile
-  // over all P V steps. Counts are in score pairs (one packed P word each).
-  constexpr int NSC = 2 * (BC / 2);
-  constexpr int EXPB_ST = FA_W_EXPB_ST < NST ? FA_W_EXPB_ST : NST;
-  constexpr int PAIRS_B = EXPB_ST * 8;                  // pairs exponentiated in block B
-  constexpr int PAIRS_C = NSC / 2 - PAIRS_B;            // pairs exponentiated in block C
-  // P V steps that carry them: all before the first step consuming P step EXPB_ST,
-  // less one, so a whole MFMA step separates the last VALU write of a P operand from
-  // the (inline assembly) MFMA that reads it
-  constexpr int C_EXP_STEPS = EXPB_ST * (D / 32) - 1;
-  constexpr int PAIRS_M = NSC / 2;                      // max pairs, over the first M_STEPS
-  constexpr int M_STEPS = NPV / 2;                      // P V steps that carry the max
-  static_assert(EXPB_ST >= 1 && (PAIRS_C == 0 || C_EXP_STEPS >= 1), "pipeline step split");
+  // ---- pipeline schedule -----------------------------------------------------------
+  // Each tile runs as two blocks of MFMA slots: the S^T MFMAs of the next tile (block
+  // B), then the P V MFMAs of this tile (block C). A slot issues one MFMA and then a
+  // batch of other instructions (LDS operand reads, copies, softmax work) that the wave
+  // issues while the matrix core executes it; slots are fenced from each other, so two
+  // MFMAs are never issued back to back (the second would stall the wave for the whole
+  // first one) and the VALU work is spread evenly over the tile.
+  //
+  // A lane holds NPAIR pairs of scores per tile (both query blocks). The softmax work
+  // of pair v is three units: the two exponentials, then the accumulation into the
+  // running sums and the 16-bit packing of the P operand. The first PAIRS_B pairs are
+  // done in block B, the rest in block C, each at least one slot before the first P V
+  // MFMA that reads them. Block C also carries the row max of the next tile (one max3
+  // per pair) and, after it, the rescale vote.
+  constexpr int SB_N = 2 * NQK;                 // slots of block B
+  constexpr int SC_N = 2 * NPV;                 // slots of block C
+  constexpr int NPAIR = BC / 2;                 // score pairs per lane and tile
+  constexpr int PAIRS_B = FA_W_PAIRS_B(D) < NPAIR ? FA_W_PAIRS_B(D) : NPAIR;
+  constexpr int UB = 3 * PAIRS_B;               // softmax units in block B
+  constexpr int UC = 3 * NPAIR - UB;            // softmax units in block C
+  // block C carries them up to two slots before the first MFMA of the last P step
+  constexpr int C_EXP_SLOTS = 2 * (NST - 1) * (D / 32) - 1;
+  constexpr int M_SLOTS = SC_N - 3;             // max units; the vote is in the next slot
+  static_assert(PAIRS_B >= NPAIR / NST, "the first P step is complete before block C");
+  static_assert(fa_wide_exp_deadlines(NPAIR, NST, D / 32, UB, C_EXP_SLOTS),
+                "every P operand is complete one slot before the MFMA that reads it");
   // K ring and V ring; slot u of a ring holds one tile at offset u * CHUNKS
   __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
   __shared__ __attribute__((aligned(1024))) u32x4_t vbuf[R * CHUNKS];
@@ -275,15 +306,12 @@ fa_fwd_wide_kernel(const Params p) {
     return *(lds_u32x4_t*)(uintptr_t)((kaddr0 ^ (uint32_t)(ds << 5)) + slot * CHUNKS * 16 +
                                       kb * 32 * CPR * 16);
   };
-  auto v_frag = [&](int slot, int i) {
+  // half h (keys 4h .. 4h+3 of each 8-key group) of the V^T operand of P V step i
+  auto v_half = [&](int slot, int i, int h) {
     const int db = i % (D / 32), st = i / (D / 32);
     const uint32_t b = vaddr[db] + slot * CHUNKS * 16;
-    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(uintptr_t)(b + (16 * st + 0) * CPR * 16));
-    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(uintptr_t)(b + (16 * st + 4) * CPR * 16));
-    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
-    return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+    return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                           (lds_s16x4_t*)(uintptr_t)(b + (16 * st + 4 * h) * CPR * 16)));
   };
 
   // S^T accumulators of one key tile: [key block][query block]; score e of a lane's
@@ -375,97 +403,104 @@ fa_fwd_wide_kernel(const Params p) {
 
   u32x4_t pb[2][NST];  // P~ of the current tile, packed as P V operands
 
-  // exponentials of flat score indices [t0, t1) of the current tile: index t is score
-  // 8 (t / 16) + t % 8 of query block (t / 8) % 2, i.e. the P operands are produced in
-  // the order the P V steps consume them (16-key step major, query block minor). The
-  // results are pinned, so they are computed in the pipeline step that calls this.
-  auto exps = [&](const STile& s, int t0, int t1) {
-#pragma unroll
-    for (int t = t0; t < t1; t += 2) {
-      const int qb = (t / 8) % 2, e = 8 * (t / 16) + t % 8;
+  // Softmax unit u of the current tile (pair v = u / 3): units 3v and 3v+1 are the two
+  // exponentials of the pair, unit 3v+2 adds them to the running sums and packs them
+  // into the P operand. Pair v is scores e, e+1 (e = 8 (v / 8) + 2 (v % 4)) of query
+  // block (v / 4) % 2, i.e. the P operands are produced in the order the P V steps
+  // consume them (16-key step major, query block minor). Results are pinned, so each
+  // unit is computed in the slot that issues it.
+  float pe[2];  // the exponentials of the pair in flight
+  auto exp_unit = [&](const STile& s, int u) {
+    const int v = u / 3, k = u % 3, qb = (v / 4) % 2, e = 8 * (v / 8) + 2 * (v % 4);
+    if (k < 2) {
       // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
-      const float p0 =
-          __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][qb][e % 16], c, -ms[qb]));
-      const float p1 =
-          __builtin_amdgcn_exp2f(__builtin_fmaf(s[e / 16][qb][(e + 1) % 16], c, -ms[qb]));
-      ls[qb][0] += p0;
-      ls[qb][1] += p1;
-      uint32_t w = E::pack(p0, p1);
-      asm volatile("" : "+v"(w));
+      pe[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[(e + k) / 16][qb][(e + k) % 16], c, -ms[qb]));
+      asm volatile("" : "+v"(pe[k]));
+    } else {
+      ls[qb][0] += pe[0];
+      ls[qb][1] += pe[1];
+      uint32_t w = E::pack(pe[0], pe[1]);
+      asm volatile("" : "+v"(w), "+v"(ls[qb][0]), "+v"(ls[qb][1]));
       pb[qb][e / 8][(e % 8) / 2] = w;
     }
-    asm volatile("" : "+v"(ls[0][0]), "+v"(ls[0][1]), "+v"(ls[1][0]), "+v"(ls[1][1]));
+  };
+  // Row max unit w of the next tile: one max3 over a pair of its scores, into one of two
+  // chains per query block.
+  auto max_unit = [&](const STile& s, float (&m)[2][2], int w) {
+    const int qb = w / (NPAIR / 2), k = w % (NPAIR / 2), e = 2 * k;
+    m[qb][k % 2] = __builtin_fmaxf(m[qb][k % 2], __builtin_fmaxf(s[e / 16][qb][e % 16],
+                                                                   s[e / 16][qb][(e + 1) % 16]));
+    asm volatile("" : "+v"(m[qb][k % 2]));
   };
 
-  // The two blocks below are software pipelines of MFMA steps. Each step is fenced
-  // with sched_barrier, so its MFMAs, its share of the VALU work and the LDS operand
-  // read for FA_W_PF steps later stay together: the matrix cores and the VALU then
-  // work side by side from one wave, which is all the latency hiding a wave that is
-  // alone on its SIMD has.
-
-  // Block B: S^T of tile j+1 (MFMA) interleaved with the first half of the
-  // exponentials of tile j (VALU) and this wave's copies of later tiles, one every
-  // NQK / NDMA steps so the four waves do not queue their copies all at once. A copy
-  // is inline assembly, which orders the LDS reads around it: it comes after its
-  // step's read.
-  static_assert(NQK % NDMA == 0, "copies spread evenly over the S^T steps");
+  // Block B: S^T of tile j+1, slot 2i + qb = step i (key block i % (BC/32), head-dim
+  // slice i / (BC/32)) for query block qb. Besides its share of the softmax units of tile
+  // j, a slot carries the K operand read for FA_W_PF steps later (after the first MFMA
+  // of a step), this wave's copies of later tiles (one every SB_N / NDMA slots, so the
+  // four waves do not queue their copies at once) and, in the last steps, the first V^T
+  // operand reads of block C.
+  static_assert(SB_N % NDMA == 0, "copies spread evenly over block B");
   auto block_b = [&](int k_next, STile& s_next, const STile& s_cur, const Copies& cp,
-                     int v_cur, u32x4_t* vpre) {
+                     int v_cur, u32x2_t (&vpre)[FA_W_PF][2]) {
     zero(s_next);
     u32x4_t kf[NQK];
 #pragma unroll
     for (int i = 0; i < FA_W_PF; ++i) kf[i] = k_frag(k_next, i);
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) {
-      if (i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(k_next, i + FA_W_PF);
-      const int kb = i % (BC / 32), ds = i / (BC / 32);
+    for (int sl = 0; sl < SB_N; ++sl) {
+      const int i = sl / 2, qb = sl % 2, kb = i % (BC / 32), ds = i / (BC / 32);
+      s_next[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_next[kb][qb]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(k_next, i + FA_W_PF);
+      if (sl % (SB_N / NDMA) == 1) copy_step(cp, sl / (SB_N / NDMA));
+      if (i >= NQK - FA_W_PF) vpre[i - (NQK - FA_W_PF)][qb] = v_half(v_cur, i - (NQK - FA_W_PF), qb);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        s_next[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_next[kb][qb]);
-      exps(s_cur, 2 * (i * PAIRS_B / NQK), 2 * ((i + 1) * PAIRS_B / NQK));
-      if (i % (NQK / NDMA) == 0) copy_step(cp, i / (NQK / NDMA));
-      // the first operand reads of the P V block run ahead across the block boundary
-      if (i >= NQK - FA_W_PF) vpre[i - (NQK - FA_W_PF)] = v_frag(v_cur, i - (NQK - FA_W_PF));
+      for (int u = sl * UB / SB_N; u < (sl + 1) * UB / SB_N; ++u) exp_unit(s_cur, u);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Block C: P V of tile j (MFMA), interleaved with the rest of the exponentials of
-  // tile j and, in its first half, the row max of tile j+1 (VALU). At the middle step
-  // the two wave halves exchange their maxima and the wave votes on the rescale, so the
-  // vote has long completed when the tile ends. Returns the row maxima of the two
-  // query blocks of tile j+1 (log2 units) and the votes.
-  auto block_c = [&](int v_cur, const STile& s_cur, const STile& s_next, const u32x4_t* vpre,
-                     float& mx0, float& mx1, uint64_t& need0, uint64_t& need1) {
+  // Block C: P V of tile j, slot 2i + qb = step i (head-dim block i % (D/32), P step
+  // i / (D/32)) for query block qb. A slot carries one half of the V^T operand read for
+  // FA_W_PF steps later, the remaining softmax units of tile j (up to two slots before
+  // their P step is read), the row max of tile j+1 and, in slot M_SLOTS, the exchange
+  // of the maxima between the two wave halves and the wave's rescale votes. Returns the
+  // row maxima of the two query blocks of tile j+1 (log2 units) and the votes.
+  auto block_c = [&](int v_cur, const STile& s_cur, const STile& s_next,
+                     const u32x2_t (&vpre)[FA_W_PF][2], float& mx0, float& mx1, uint64_t& need0,
+                     uint64_t& need1) {
     float m[2][2] = {{-__builtin_inff(), -__builtin_inff()},
                      {-__builtin_inff(), -__builtin_inff()}};
-    u32x4_t vf[NPV];
+    u32x2_t vh[NPV][2];
 #pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) vf[i] = vpre[i];
+    for (int i = 0; i < FA_W_PF; ++i) {
+      vh[i][0] = vpre[i][0];
+      vh[i][1] = vpre[i][1];
+    }
 #pragma unroll
-    for (int i = 0; i < NPV; ++i) {
+    for (int sl = 0; sl < SC_N; ++sl) {
+      const int i = sl / 2, qb = sl % 2, db = i % (D / 32), st = i / (D / 32);
       // The compiler does not know the MFMAs below read their sources over several
       // cycles (they are inline assembly): keep the previous step's sources live
-      // until this step, so no VALU result is written into them right behind the MFMA.
-      if (i > 0) asm volatile("" ::"v"(vf[i - 1]), "v"(pb[0][(i - 1) / (D / 32)]),
-                              "v"(pb[1][(i - 1) / (D / 32)]));
-      if (i + FA_W_PF < NPV) vf[i + FA_W_PF] = v_frag(v_cur, i + FA_W_PF);
-      const int db = i % (D / 32), st = i / (D / 32);
+      // until this step, so no result is written into them right behind the MFMA.
+      if (qb == 0 && i > 0)
+        asm volatile("" ::"v"(vh[i - 1][0]), "v"(vh[i - 1][1]), "v"(pb[0][(i - 1) / (D / 32)]),
+                     "v"(pb[1][(i - 1) / (D / 32)]));
+      const u32x4_t vf = {vh[i][0][0], vh[i][0][1], vh[i][1][0], vh[i][1][1]};
+      mfma_acc_agpr<BF16>(oacc[db][qb], vf, pb[qb][st]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + FA_W_PF < NPV) vh[i + FA_W_PF][qb] = v_half(v_cur, i + FA_W_PF, qb);
+      if (sl < C_EXP_SLOTS) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) mfma_acc_agpr<BF16>(oacc[db][qb], vf[i], pb[qb][st]);
-      if (i < C_EXP_STEPS)
-        exps(s_cur, 2 * PAIRS_B + 2 * (i * PAIRS_C / C_EXP_STEPS),
-             2 * PAIRS_B + 2 * ((i + 1) * PAIRS_C / C_EXP_STEPS));
-      if (i < M_STEPS) {
-#pragma unroll
-        for (int t = 2 * (i * PAIRS_M / M_STEPS); t < 2 * ((i + 1) * PAIRS_M / M_STEPS); t += 2) {
-          const int qb = t / (BC / 2), e = t % (BC / 2);
-          m[qb][0] = __builtin_fmaxf(m[qb][0], s_next[e / 16][qb][e % 16]);
-          m[qb][1] = __builtin_fmaxf(m[qb][1], s_next[e / 16][qb][(e + 1) % 16]);
-        }
-        asm volatile("" : "+v"(m[0][0]), "+v"(m[0][1]), "+v"(m[1][0]), "+v"(m[1][1]));
+        for (int u = sl * UC / C_EXP_SLOTS; u < (sl + 1) * UC / C_EXP_SLOTS; ++u)
+          exp_unit(s_cur, UB + u);
       }
-      if (i == M_STEPS) {
+      if (sl < M_SLOTS) {
+#pragma unroll
+        for (int w = sl * NPAIR / M_SLOTS; w < (sl + 1) * NPAIR / M_SLOTS; ++w)
+          max_unit(s_next, m, w);
+      }
+      if (sl == M_SLOTS) {
         mx0 = xhalf_max(__builtin_fmaxf(m[0][0], m[0][1])) * c;
         mx1 = xhalf_max(__builtin_fmaxf(m[1][0], m[1][1])) * c;
         need0 = __builtin_amdgcn_ballot_w64(mx0 > ms[0] + p.tau);
@@ -482,7 +517,7 @@ fa_fwd_wide_kernel(const Params p) {
   // holds a stale or clamped tile, and its result is dropped (`next` false).
   auto tile = [&](const STile& s_cur, STile& s_next, int k_next, int v_cur, int j, bool next,
                   const Copies& cp) {
-    u32x4_t vpre[FA_W_PF];
+    u32x2_t vpre[FA_W_PF][2];
     block_b(k_next, s_next, s_cur, cp, v_cur, vpre);
     mask(s_next, j + 1);
     float mx0, mx1;
