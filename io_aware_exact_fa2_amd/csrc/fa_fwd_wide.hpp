@@ -591,6 +591,10 @@ fa_fwd_wide_kernel(const Params p) {
     }
   }
 
+  // The last iterations' copies (of clamped tiles that no iteration reads) may still be
+  // in flight: let them land before the workgroup can end and its LDS be reassigned.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
   if (!wave_live) return;
   const float kLn2 = 0.69314718055994530942f;
