@@ -171,8 +171,8 @@ def cpu_baseline(w, budget_s: float):
     dt = time.perf_counter() - t0
     flops = w.flops() * done / len(heads)
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": workers, "kind": "oracle",
-            "sample": f"{done} (b,h) heads of {w.name} ({len(heads)} per batch), all {w.N} "
-                      f"rows each, float64 numpy, {dt:.1f} s"}
+            "sample": f"{done} whole-head passes (all {w.N} rows each) cycling over the "
+                      f"{len(heads)} (b,h) heads of {w.name}, float64 numpy, {dt:.1f} s"}
 
 
 def main(argv=None):
