@@ -90,6 +90,47 @@ def time_gpu(w, steps, warmup):
     return ms, wall, ran
 
 
+def time_cold(w, steps, scrub_mib=512):
+    """Median kernel time with a scrub write of scrub_mib MiB before every launch, so Q, K
+    and V come from HBM rather than the L2 / MALL (events bracket the launch only)."""
+    import torch
+    import io_aware_exact_fa2_amd as fa
+    import workloads
+
+    q, k, v = (t.to("cuda:0") for t in workloads.make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    scrub = torch.empty(scrub_mib << 20, dtype=torch.uint8, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_fp16
+    args = (q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream)
+    times = []
+    for _ in range(steps):
+        scrub.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = fn(*args)
+        e1.record(stream)
+        if st != fa.FA_OK:
+            raise fa.FAError(st)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def calibrate_copy(mib: int):
     """A plain device copy of known size (float32 multiply by 1, out of place) whose
     FETCH_SIZE / WRITE_SIZE counters calibrate the attention kernel's traffic."""
@@ -182,6 +223,7 @@ def cpu_baseline(w, budget_s: float):
     dt = time.perf_counter() - t0
     flops = w.flops() * done / len(heads)
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done} whole-head passes (all {w.N} rows each) cycling over the "
                       f"{len(heads)} (b,h) heads of {w.name}, float64 numpy, {dt:.1f} s"}
 
@@ -228,6 +270,9 @@ def main(argv=None):
     traffic = measured_traffic(w.name)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": traffic}
+    ms_cold = time_cold(w, 10)
+    cold = {"ms": round(ms_cold, 4), "tflops": round(w.flops() / (ms_cold * 1e-3) / 1e12, 1),
+            "scrub_mib": 512, "statistic": "median of 10 launches, each after the scrub"}
     extra = {}
     for name in [s for s in a.also.split(",") if s]:
         wx = workloads.get(name)
@@ -259,6 +304,7 @@ def main(argv=None):
         "wall_s_timed": round(wall, 4),
         "kernel_source_sha256_16": kernel_hash(),
         "roofline": roof,
+        "cold": cold,
         "workloads": extra,
     }
     if a.cpu_budget > 0:
