@@ -192,11 +192,15 @@ fa_fwd_wide_kernel(const Params p) {
   const uint16_t* __restrict__ vg = p.v + head;
 
   const int q0 = qt * G::BR;
-  const int wq0 = q0 + wid * 64;
+  // The workgroup's 256 queries are eight 32-query blocks; wave w owns blocks w and 7 - w
+  // (query block qb = 0, 1 of the wave), so under the causal mask the four waves end
+  // their rows within one key tile of each other.
+  const int qbase[2] = {q0 + 32 * wid, q0 + 32 * (2 * NW - 1 - wid)};
+  const int wq0 = qbase[0];  // the wave's first query
   const int q_end = min(q0 + G::BR, N);
   const int n_kt = CAUSAL ? (q_end + BC - 1) / BC : (N + BC - 1) / BC;
   const bool wave_live = wq0 < N;
-  const int w_last_q = min(wq0 + 64, N) - 1;
+  const int w_last_q = min(qbase[1] + 32, N) - 1;
   const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
 
   // ---- HBM -> LDS copies ---------------------------------------------------------
@@ -250,7 +254,7 @@ fa_fwd_wide_kernel(const Params p) {
   u32x4_t qf[2][D / 16];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qi = min(wq0 + 32 * qb + l32, N - 1);
+    const int qi = min(qbase[qb] + l32, N - 1);
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds)
       qf[qb][ds] = global_load16(qg + (size_t)qi * D + ds * 16 + hh * 8);
@@ -360,7 +364,7 @@ fa_fwd_wide_kernel(const Params p) {
         if (kb + qb > 0) asm volatile("" : "+v"(s[kb][qb]));
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int last = CAUSAL ? min(N - 1, wq0 + 32 * qb + l32) : N - 1;
+      const int last = CAUSAL ? min(N - 1, qbase[qb] + l32) : N - 1;
       const int t = last - base;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
@@ -602,7 +606,7 @@ fa_fwd_wide_kernel(const Params p) {
   for (int qb = 0; qb < 2; ++qb) {
     drain_o(qb);
     const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
-    const int qi = wq0 + 32 * qb + l32;
+    const int qi = qbase[qb] + l32;
     if (qi < N) {
       const float inv = 1.0f / l_tot;
       uint16_t* orow = p.o + head + (size_t)qi * D;

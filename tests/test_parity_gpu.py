@@ -136,6 +136,10 @@ REDUCED = [
     ("stress_causal", 1, 2, 777, 64, "fp16", True, "stress"),
     ("d64_bf16_causal", 1, 3, 333, 64, "bf16", True, "normal"),
     ("d128_fp16", 1, 2, 300, 128, "fp16", False, "normal"),
+    # causal with a last query tile that is only partly inside N: some of a wave's two
+    # 32-query blocks are valid, some are not
+    ("d128_causal_ragged_fp16", 1, 2, 300, 128, "fp16", True, "normal"),
+    ("d128_causal_short_tail", 2, 2, 260, 128, "bf16", True, "normal"),
 ]
 
 
