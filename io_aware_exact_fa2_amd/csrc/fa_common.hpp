@@ -29,6 +29,7 @@ struct Params {
   uint32_t qsign; // 0x80008000 when scale < 0: Q is negated on load (exact), else 0
   int xcd_map;    // 1 when BH % 8 == 0: the heads of one XCD stay on it
   float tau;      // rescale threshold in log2 units (fast kernel; 0: every tile)
+  int next_stride;  // > 0: workgroup b warms the L2 with the Q tile of workgroup b + next_stride
 };
 
 // --- element type -----------------------------------------------------------------

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -42,6 +43,9 @@ thread_local int g_last_hip_error = 0;
 #ifndef FA_WIDE_RING
 #define FA_WIDE_RING 4    // LDS ring slots per tensor
 #endif
+#ifndef FA_WIDE_WARM
+#define FA_WIDE_WARM 1  // warm the L2 with the next round's Q tiles
+#endif
 #ifndef FA_WIDE_BC
 #define FA_WIDE_BC 64
 #endif
@@ -51,6 +55,20 @@ constexpr int kQB = 1;                    //               32-query blocks per w
 constexpr int kBC = 64;                   //               keys per tile
 constexpr int kGBR = kNW * kQB * 32;      //               queries per workgroup
 constexpr int kMinBR = kFNW * 32 < kGBR ? kFNW * 32 : kGBR;   // smallest query tile
+
+// CU count of the current device, read once per device (immutable afterwards).
+int cu_count() {
+  static std::once_flag once[64];
+  static int count[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::call_once(once[dev], [dev]() {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    count[dev] = n;
+  });
+  return count[dev];
+}
 
 bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
@@ -104,6 +122,8 @@ hipError_t launch_wide(fa::Params p, hipStream_t stream) {
   using G = fa::WideGeom<D, FA_WIDE_BC, FA_WIDE_RING>;
   p.n_qt = (p.N + G::BR - 1) / G::BR;
   const int grid = p.n_qt * p.BH;
+  // one workgroup per CU at a time: workgroup b + (CU count) is the next one on b's XCD
+  if (FA_WIDE_WARM) p.next_stride = cu_count();
   auto kern = fa::fa_fwd_wide_kernel<BF16, D, CAUSAL, FA_WIDE_BC, FA_WIDE_RING>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(G::NW * 64), 0, stream, p);
   return hipGetLastError();
@@ -138,6 +158,7 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
   p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
   p.tau = tau;
+  p.next_stride = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;

@@ -176,6 +176,8 @@ fa_fwd_wide_kernel(const Params p) {
   // K ring and V ring; slot u of a ring holds one tile at offset u * CHUNKS
   __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
   __shared__ __attribute__((aligned(1024))) u32x4_t vbuf[R * CHUNKS];
+  // landing area of the L2-warming copies below (their data is never read)
+  __shared__ __attribute__((aligned(1024))) u32x4_t warm[NW * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -577,6 +579,47 @@ fa_fwd_wide_kernel(const Params p) {
   wait_ring();  // K_1 and V_0
   ring_barrier();  // and every wave is done with slot 0 of K before K_R overwrites it
 
+  // ---- warming the L2 for the next workgroup --------------------------------------------
+  // The hardware starts workgroup b + next_stride (the next round, same XCD, hence the
+  // same L2) when a workgroup of this round ends, and every workgroup of a round would
+  // fetch its 64 KB of Q from HBM at the same moment. So three tiles before its end this
+  // workgroup copies that Q tile, and the first K tile of its head (the next workgroup
+  // waits for both before its first MFMA), through the L2 into a scratch area of LDS;
+  // the next workgroup then finds them in the cache. The copies join the ring's memory
+  // counter: the waits of that iteration and the next leave them in flight as well.
+  constexpr int WARM_Q = D / 8;   // 64 rows of Q per wave, 1 KB per copy
+  constexpr int WARM_K = D / 32;  // 16 rows of K_0 per wave
+  constexpr int WARM_OPS = WARM_Q + WARM_K;
+  const int next_item = p.next_stride > 0 ? (int)blockIdx.x + p.next_stride : -1;
+  const bool do_warm = next_item >= 0 && next_item < p.n_qt * p.BH && n_kt >= 4;
+  const int j_warm = n_kt - 3;
+  // buffer over `rows` rows of src from row r0 (rows past N read as zeros), wave-uniform:
+  // read from the first lane so it stays in scalar registers
+  auto rows_rsrc = [&](const uint16_t* src, int r0, int rows) {
+    const u32x4_t r4 = buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)min(r0, N - 1) * D),
+                                   (uint32_t)(max(min(N - r0, rows), 0) * D * 2));
+    return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(r4[0]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(r4[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(r4[2]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(r4[3])};
+  };
+  auto warm_next = [&]() {
+    int bh2, qt2;
+    decode_tile<CAUSAL>(p, next_item, bh2, qt2);
+    const size_t head2 = (size_t)bh2 * (size_t)N * D;
+    const u32x4_t rq = rows_rsrc(p.q + head2, qt2 * G::BR + wid * 64, 64);
+    const u32x4_t rk = rows_rsrc(p.k + head2, wid * (BC / NW), BC / NW);
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(warm + wid * 64));
+    const uint32_t off = (uint32_t)lane * 16u;  // 1 KB per copy: 64 lanes x 16 B
+#pragma unroll
+    for (int i = 0; i < WARM_Q; ++i) lds_copy16(rq, off + 1024u * i, lds, 0);
+#pragma unroll
+    for (int i = 0; i < WARM_K; ++i) lds_copy16(rk, off + 1024u * i, lds, 0);
+  };
+  static_assert(D * 2 * 64 == WARM_Q * 1024 && D * 2 * (BC / NW) == WARM_K * 1024,
+                "one wave's rows are whole 1 KB copies");
+  static_assert(NDMA * (R - 2) + WARM_OPS <= 63, "outstanding copies fit the vmcnt field");
+
   // ---- main loop: slots of tile j are j % R (K and V), unrolled over the ring --------
   for (int j0 = 0; j0 < n_kt; j0 += R) {
 #pragma unroll
@@ -586,11 +629,15 @@ fa_fwd_wide_kernel(const Params p) {
       const Copies cp = {u, (u + R - 1) % R, j + R, j + R - 1};
       STile& s_cur = (u % 2 == 0) ? sa : sb;
       STile& s_nxt = (u % 2 == 0) ? sb : sa;
+      if (do_warm && j == j_warm) warm_next();
       if (wave_live && j < w_kt)
         tile(s_cur, s_nxt, (u + 1) % R, u, j, j + 1 < w_kt, cp);
       else
         copy_all(cp);
-      wait_ring();
+      if (do_warm && (j == j_warm || j == j_warm + 1))
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * (R - 2) + WARM_OPS) : "memory");
+      else
+        wait_ring();
       ring_barrier();
     }
   }
