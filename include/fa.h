@@ -8,9 +8,12 @@
  *  [P3] ariser.io, "FlashAttention: 어텐션을 빠르게 만든 건 계산량보다 데이터
  *       이동이었다"
  *
- * The library is stateless: it never allocates device memory, keeps no pointer
- * after a call returns and needs no workspace (the O(N) extra memory of the
- * [P1] "정리" comparison table is the L output itself). Calls are reentrant and
+ * The library never allocates device memory, keeps no pointer after a call returns
+ * and needs no workspace (the O(N) extra memory of the [P1] "정리" comparison table
+ * is the L output itself). Its only global state is the compute-unit count of each
+ * device, read once per device (std::call_once) and immutable afterwards; it only
+ * steers which of the call's own Q and K rows a workgroup pre-loads into the L2 (a
+ * performance hint, never a correctness input). Calls are reentrant and
  * thread-safe. No C++ exception crosses this boundary.
  */
 #ifndef FA_H_
