@@ -42,6 +42,9 @@
 #ifndef FA_W_PF
 #define FA_W_PF 2         // MFMA steps an LDS operand read runs ahead
 #endif
+#ifndef FA_W_KPRE
+#define FA_W_KPRE 1       // first K operands of a tile read at the end of the previous one
+#endif
 #ifndef FA_W_PAIRS_B128
 #define FA_W_PAIRS_B128 19  // score pairs (of 32) exponentiated in the S^T block, d = 128
 #endif
@@ -446,12 +449,13 @@ fa_fwd_wide_kernel(const Params p) {
   // four waves do not queue their copies at once) and, in the last steps, the first V^T
   // operand reads of block C.
   static_assert(SB_N % NDMA == 0, "copies spread evenly over block B");
+  u32x4_t kpre[FA_W_PF];  // the first K operands of the next block B
   auto block_b = [&](int k_next, STile& s_next, const STile& s_cur, const Copies& cp,
                      int v_cur, u32x2_t (&vpre)[FA_W_PF][2]) {
     zero(s_next);
     u32x4_t kf[NQK];
 #pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) kf[i] = k_frag(k_next, i);
+    for (int i = 0; i < FA_W_PF; ++i) kf[i] = FA_W_KPRE ? kpre[i] : k_frag(k_next, i);
 #pragma unroll
     for (int sl = 0; sl < SB_N; ++sl) {
       const int i = sl / 2, qb = sl % 2, kb = i % (BC / 32), ds = i / (BC / 32);
@@ -472,7 +476,10 @@ fa_fwd_wide_kernel(const Params p) {
   // their P step is read), the row max of tile j+1 and, in slot M_SLOTS, the exchange
   // of the maxima between the two wave halves and the wave's rescale votes. Returns the
   // row maxima of the two query blocks of tile j+1 (log2 units) and the votes.
-  auto block_c = [&](int v_cur, const STile& s_cur, const STile& s_next,
+  // The last slots, which read no V^T operands, read the first K operands of the next
+  // tile's block B (K slot k_after), so that block starts without an LDS wait.
+  static_assert(2 * (NPV - FA_W_PF) + 2 * FA_W_PF <= SC_N, "slots for the K look-ahead");
+  auto block_c = [&](int v_cur, int k_after, const STile& s_cur, const STile& s_next,
                      const u32x2_t (&vpre)[FA_W_PF][2], float& mx0, float& mx1, uint64_t& need0,
                      uint64_t& need1) {
     float m[2][2] = {{-__builtin_inff(), -__builtin_inff()},
@@ -496,6 +503,7 @@ fa_fwd_wide_kernel(const Params p) {
       mfma_acc_agpr<BF16>(oacc[db][qb], vf, pb[qb][st]);
       __builtin_amdgcn_sched_barrier(0);
       if (i + FA_W_PF < NPV) vh[i + FA_W_PF][qb] = v_half(v_cur, i + FA_W_PF, qb);
+      if (FA_W_KPRE && qb == 0 && i >= NPV - FA_W_PF) kpre[i - (NPV - FA_W_PF)] = k_frag(k_after, i - (NPV - FA_W_PF));
       if (sl < C_EXP_SLOTS) {
 #pragma unroll
         for (int u = sl * UC / C_EXP_SLOTS; u < (sl + 1) * UC / C_EXP_SLOTS; ++u)
@@ -521,24 +529,27 @@ fa_fwd_wide_kernel(const Params p) {
   // ms: exponentials and P V of tile j, overlapped with the S^T, mask and max of tile
   // j+1 (from K slot k_next). On a wave's last tile the look-ahead reads a slot that
   // holds a stale or clamped tile, and its result is dropped (`next` false).
-  auto tile = [&](const STile& s_cur, STile& s_next, int k_next, int v_cur, int j, bool next,
-                  const Copies& cp) {
+  auto tile = [&](const STile& s_cur, STile& s_next, int k_next, int v_cur, int k_after, int j,
+                  bool next, const Copies& cp) {
     u32x2_t vpre[FA_W_PF][2];
     block_b(k_next, s_next, s_cur, cp, v_cur, vpre);
     mask(s_next, j + 1);
     float mx0, mx1;
     uint64_t need0, need1;
-    block_c(v_cur, s_cur, s_next, vpre, mx0, mx1, need0, need1);
+    block_c(v_cur, k_after, s_cur, s_next, vpre, mx0, mx1, need0, need1);
     if (next) {
       grow_max(0, mx0, need0);
       grow_max(1, mx1, need1);
     }
   };
 
-  // After this wave's copies for tiles up to (K_{j+2}, V_{j+1}) have landed, the newest
-  // R - 2 iterations of copies may still be in flight.
+  // After this wave's copies for tiles up to (K_{j+2}, V_{j+1}) have landed (and
+  // K_{j+3}, whose first operands the next tile reads ahead), the newest RING_LAG
+  // iterations of copies may still be in flight.
+  constexpr int RING_LAG = FA_W_KPRE ? R - 3 : R - 2;
+  static_assert(RING_LAG >= 0, "ring deep enough for the K look-ahead");
   auto wait_ring = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * (R - 2)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * RING_LAG) : "memory");
   };
   // Workgroup barrier for the ring. This wave's LDS reads are complete before it
   // (lgkmcnt), so after it another wave may overwrite the slots they read; copies
@@ -576,8 +587,12 @@ fa_fwd_wide_kernel(const Params p) {
       ms[qb] = xhalf_max(mx) * c;
     }
   }
-  wait_ring();  // K_1 and V_0
+  wait_ring();  // K_1 and V_0 (and K_2, V_1 with the K look-ahead)
   ring_barrier();  // and every wave is done with slot 0 of K before K_R overwrites it
+  if (FA_W_KPRE) {
+#pragma unroll
+    for (int i = 0; i < FA_W_PF; ++i) kpre[i] = k_frag(1, i);  // tile 0's block B: K_1
+  }
 
   // ---- warming the L2 for the next workgroup --------------------------------------------
   // The hardware starts workgroup b + next_stride (the next round, same XCD, hence the
@@ -618,7 +633,7 @@ fa_fwd_wide_kernel(const Params p) {
   };
   static_assert(D * 2 * 64 == WARM_Q * 1024 && D * 2 * (BC / NW) == WARM_K * 1024,
                 "one wave's rows are whole 1 KB copies");
-  static_assert(NDMA * (R - 2) + WARM_OPS <= 63, "outstanding copies fit the vmcnt field");
+  static_assert(NDMA * RING_LAG + WARM_OPS <= 63, "outstanding copies fit the vmcnt field");
 
   // ---- main loop: slots of tile j are j % R (K and V), unrolled over the ring --------
   for (int j0 = 0; j0 < n_kt; j0 += R) {
@@ -631,11 +646,11 @@ fa_fwd_wide_kernel(const Params p) {
       STile& s_nxt = (u % 2 == 0) ? sb : sa;
       if (do_warm && j == j_warm) warm_next();
       if (wave_live && j < w_kt)
-        tile(s_cur, s_nxt, (u + 1) % R, u, j, j + 1 < w_kt, cp);
+        tile(s_cur, s_nxt, (u + 1) % R, u, (u + 2) % R, j, j + 1 < w_kt, cp);
       else
         copy_all(cp);
       if (do_warm && (j == j_warm || j == j_warm + 1))
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * (R - 2) + WARM_OPS) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * RING_LAG + WARM_OPS) : "memory");
       else
         wait_ring();
       ring_barrier();
