@@ -25,12 +25,16 @@ Modules:
 * ``bruteforce`` — pure-Python loops without the max shift, for tiny inputs.
 * ``online``     — the pages' algorithm steps (scalar online softmax, block
   merge, FA2 and FA1 loop orders) in float64, used to pin the pages' claims.
+* ``backward``   — the gradients of the same definition (dQ, dK, dV) in float64,
+  the reference for the backward pass that recomputes P from L.
 
 Every function here is pinned by ``tests/test_oracle_pins.py``; none is
 "parity unpinned".
 """
 from .attention import attention, attention_rows
 from .bruteforce import attention_bruteforce
+from .backward import attention_backward
 from . import online
 
-__all__ = ["attention", "attention_rows", "attention_bruteforce", "online"]
+__all__ = ["attention", "attention_rows", "attention_bruteforce", "attention_backward",
+           "online"]

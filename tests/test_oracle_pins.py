@@ -407,3 +407,99 @@ def test_planted_mistakes_are_caught():
         assert np.abs(L - ref_L).max() > 1e-3, name
     O_unnorm = np.exp(S - S.max(1, keepdims=True)) @ v[0, 0]
     assert np.abs(O_unnorm - ref_O).max() > 1e-3
+
+
+# ------------------------------------------------------------------ backward (NEXT-1)
+# oracle.attention_backward is the chain rule written out; these pins fix it with
+# things other than itself: a library's automatic differentiation of the forward
+# definition, finite differences of the (pinned) forward oracle, closed forms and
+# identities of the softmax Jacobian.
+
+def _bwd_inputs(B, H, N, d, seed):
+    return (_rand((B, H, N, d), seed), _rand((B, H, N, d), seed + 1),
+            _rand((B, H, N, d), seed + 2), _rand((B, H, N, d), seed + 3))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_autograd(causal):
+    """torch's float64 autograd of the plain forward formula (a library routine)."""
+    import torch
+    q, k, v, do = _bwd_inputs(2, 2, 11, 5, 300)
+    scale = 0.7
+    tq, tk, tv = (torch.tensor(t, requires_grad=True) for t in (q, k, v))
+    s = scale * tq @ tk.transpose(-1, -2)
+    if causal:
+        n = s.shape[-1]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ tv
+    (o * torch.tensor(do)).sum().backward()
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    """Central differences of sum(O * dO) through the forward oracle (itself pinned)."""
+    q, k, v, do = _bwd_inputs(1, 1, 6, 4, 310)
+    scale = 0.9
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention(q_, k_, v_, scale, causal, workers=1)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    rng = np.random.Generator(np.random.PCG64(311))
+    for which, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(6):
+            idx = (0, 0, int(rng.integers(6)), int(rng.integers(4)))
+            args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+            args[which][idx] += eps
+            up = loss(args["q"], args["k"], args["v"])
+            args[which][idx] -= 2 * eps
+            dn = loss(args["q"], args["k"], args["v"])
+            assert abs((up - dn) / (2 * eps) - grad[idx]) < 1e-7, (which, idx)
+
+
+def test_backward_uniform_scores_closed_form():
+    """Q = 0: P_ij = 1/N, so dV_j = mean_i dO_i, dK = 0 and
+    dQ_i = scale/N * sum_j <dO_i, V_j - mean V> K_j."""
+    _, k, v, do = _bwd_inputs(1, 2, 7, 3, 320)
+    q = np.zeros_like(k)
+    scale = 1.3
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, False)
+    n = q.shape[2]
+    vbar = v.mean(axis=2, keepdims=True)
+    want_dv = np.broadcast_to(do.mean(axis=2, keepdims=True), dv.shape)
+    w = np.einsum("bhid,bhjd->bhij", do, v - vbar)
+    want_dq = scale / n * np.einsum("bhij,bhjd->bhid", w, k)
+    np.testing.assert_allclose(dv, want_dv, atol=1e-13)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dq, want_dq, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_row_sums_vanish(causal):
+    """Each row of dS sums to 0 (the softmax Jacobian annihilates constants): with all
+    keys equal, dQ = scale * sum_j dS_ij K = 0; and the causal row 0 (one allowed key,
+    P = 1) gets dQ_0 = 0 whatever its inputs."""
+    q, _, v, do = _bwd_inputs(1, 1, 9, 4, 330)
+    k = np.broadcast_to(_rand((1, 1, 1, 4), 331), q.shape).copy()
+    dq, _, _ = oracle.attention_backward(q, k, v, do, 0.8, causal)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-13)
+    q, k, v, do = _bwd_inputs(1, 1, 9, 4, 332)
+    dq, _, _ = oracle.attention_backward(q, k, v, do, 0.8, True)
+    np.testing.assert_allclose(dq[0, 0, 0], 0.0, atol=1e-13)
+
+
+def test_backward_linear_in_do():
+    """The gradients are linear in dO (a planted sign or scale mistake breaks this)."""
+    q, k, v, do = _bwd_inputs(1, 1, 8, 4, 340)
+    do2 = _rand(do.shape, 341)
+    a = oracle.attention_backward(q, k, v, do, 0.6, False)
+    b = oracle.attention_backward(q, k, v, do2, 0.6, False)
+    c = oracle.attention_backward(q, k, v, 2.0 * do - 3.0 * do2, 0.6, False)
+    for x, y, z in zip(a, b, c):
+        np.testing.assert_allclose(z, 2.0 * x - 3.0 * y, atol=1e-12)
