@@ -1,5 +1,6 @@
 /*
- * fa.h — C ABI of the FA2-order attention forward pass for AMD MI355X (gfx950).
+ * fa.h — C ABI of the FA2-order attention forward pass, and of its backward
+ * pass, for AMD MI355X (gfx950).
  *
  * Sources for the operation (web pages on FlashAttention):
  *  [P1] currybab.bearblog.dev, "Triton으로 FlashAttention 구현하기 전에 -
@@ -7,6 +8,8 @@
  *  [P2] iq-universe.github.io, "FlashAttention은 어떻게 O(N²) 메모리 벽을 넘었나"
  *  [P3] ariser.io, "FlashAttention: 어텐션을 빠르게 만든 건 계산량보다 데이터
  *       이동이었다"
+ *  [P2'] iq-universe.github.io, "FlashAttention: SRAM tiling으로 O(N²) HBM을
+ *       우회하다" (the chapter's second page)
  *
  * The library never allocates device memory, keeps no pointer after a call returns
  * and needs no workspace (the O(N) extra memory of the [P1] "정리" comparison table
@@ -125,6 +128,57 @@ int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               float rescale_log2, void* stream);
+
+/*
+ * fa_bwd — gradients of the attention of fa_fwd with respect to q, k and v,
+ * bfloat16 tensors.
+ *
+ * For the loss sum_{b,h,i,c} O[b,h,i,c] * dO[b,h,i,c] (so dout is dLoss/dO), per
+ * batch and head, with P the softmax of fa_fwd over the allowed keys:
+ *
+ *   dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO[i,c] * O[i,c],
+ *   dS = P * (dP - D)   (elementwise, D broadcast along each row),
+ *   dQ = scale * dS K,   dK = scale * dS^T Q.
+ *
+ * P is not stored by the forward pass: it is recomputed block by block as
+ * P_ij = exp(S_ij - lse_i) ([P1] FA2 section, the LSE identity; [P2'] the
+ * paragraph on activation memory; [P3] "계산을 다시 하는 편이 싸다는 역설", which
+ * trades that recomputation for the N x N matrix's HBM traffic). D_i equals
+ * rowsum(P * dP) (the softmax Jacobian), computed from dO and O.
+ *
+ * Arguments
+ *   q, k, v  the inputs of the forward call: [B, H, N, d] bfloat16, row-major,
+ *            contiguous, 16-byte aligned (read only; they may alias each other).
+ *   o, lse   fa_fwd's outputs for q, k, v with the same scale and causal
+ *            ([B, H, N, d] bfloat16 and [B, H, N] float32; read only). Other
+ *            values give the gradients of a different function (unspecified).
+ *   dout     dLoss/dO, [B, H, N, d] bfloat16 (read only), 16-byte aligned.
+ *   dq, dk, dv  outputs, [B, H, N, d] bfloat16, written with round-to-nearest-
+ *            even; 16-byte aligned; each written by exactly one workgroup.
+ *   B, H, N  each >= 1.
+ *   d        64 or 128 (FA_ERR_UNSUPPORTED otherwise).
+ *   scale, causal  as passed to fa_fwd.
+ *   stream   a hipStream_t passed as void*; NULL means the default stream.
+ *
+ * Ownership: the caller allocates and frees every buffer; no workspace is used.
+ * dq, dk and dv may overlap neither each other nor any input. Size limits are
+ * those of fa_fwd.
+ *
+ * Errors and asynchrony: as fa_fwd (validation on the host before any HIP call;
+ * FA_ERR_HIP with fa_last_hip_error() when a launch is refused; the call only
+ * enqueues two kernels on `stream`).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+           float scale, int causal, void* stream);
+
+/*
+ * fa_bwd_fp16 — the same operation, arguments and contract as fa_bwd, for IEEE
+ * float16 q, k, v, o, dout, dq, dk, dv (lse stays float32).
+ */
+int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                float scale, int causal, void* stream);
 
 /*
  * fa_fwd_supported — 1 if a call with this head dimension, dtype code

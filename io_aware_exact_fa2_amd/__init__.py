@@ -1,14 +1,15 @@
-"""FA2-order exact attention forward for AMD MI355X (gfx950).
+"""FA2-order exact attention (forward and backward) for AMD MI355X (gfx950).
 
 Thin Python binding of the C ABI in ``include/fa.h`` (``libfa.so``, built from
 ``csrc/`` by ``build.py``). It only marshals arguments: every step of the
 computation runs in the HIP kernel. PyTorch supplies device buffers and the
 stream. There is no fallback: if the library is missing, every call raises.
 
-Functions with the C names (``fa_fwd``, ``fa_fwd_fp16``, ``fa_fwd_supported``,
-``fa_strerror``, ``fa_last_hip_error``, ``fa_version``) map 1:1 onto the C
-entry points; ``forward`` is the tensor-level convenience that allocates O and
-L and raises ``FAError`` on a nonzero status.
+Functions with the C names (``fa_fwd``, ``fa_fwd_fp16``, ``fa_fwd_ex``,
+``fa_bwd``, ``fa_bwd_fp16``, ``fa_fwd_supported``, ``fa_strerror``,
+``fa_last_hip_error``, ``fa_version``) map 1:1 onto the C entry points;
+``forward`` and ``backward`` are the tensor-level conveniences that allocate the
+outputs and raise ``FAError`` on a nonzero status.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIAS",
     "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError",
     "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
+    "fa_bwd", "fa_bwd_fp16", "backward",
     "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
 ]
@@ -34,8 +36,8 @@ FA_ERR_HIP = -6
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported", "fa_strerror",
-           "fa_last_hip_error", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
+           "fa_strerror", "fa_last_hip_error", "fa_version")
 FA_DEFAULT_RESCALE_LOG2 = 8.0
 FA_MAX_RESCALE_LOG2 = 15.0
 
@@ -74,6 +76,10 @@ def lib() -> ctypes.CDLL:
         fn.restype = i
     L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, vp]
     L.fa_fwd_ex.restype = i
+    for name in ("fa_bwd", "fa_bwd_fp16"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        fn.restype = i
     L.fa_fwd_supported.argtypes = [i, i, i]
     L.fa_fwd_supported.restype = i
     L.fa_strerror.argtypes = [i]
@@ -118,6 +124,21 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, rescale_log2,
     return lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                            float(scale), int(causal), int(dtype), float(rescale_log2),
                            _stream(stream))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream=None) -> int:
+    """C ``fa_bwd`` (bfloat16). Pointers may be tensors or raw integers."""
+    return lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                        _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(causal),
+                        _stream(stream))
+
+
+def fa_bwd_fp16(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
+                stream=None) -> int:
+    """C ``fa_bwd_fp16`` (float16). Pointers may be tensors or raw integers."""
+    return lib().fa_bwd_fp16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                             _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                             int(causal), _stream(stream))
 
 
 def fa_fwd_supported(d: int, dtype: int, causal: int) -> int:
@@ -181,3 +202,43 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None,
     if st != FA_OK:
         raise FAError(st, name)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, stream=None):
+    """dQ, dK, dV for contiguous [B, H, N, d] bf16/fp16 CUDA tensors (d = 64 or 128).
+
+    o and lse are ``forward``'s outputs for the same q, k, v, causal and scale; dout
+    is the gradient of the loss with respect to o. The gradients have q's dtype.
+    """
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("q, k, v, o, dout must share dtype bfloat16 or float16")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must have the same [B, H, N, d] shape")
+    if not q.is_cuda or any(t.device != q.device for t in (*ts, lse)):
+        raise ValueError("all tensors must be on the same GPU")
+    if not all(t.is_contiguous() for t in (*ts, lse)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for t in (dq, dk, dv):
+        if t is None:
+            t = torch.empty_like(q)
+        elif t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous tensors like q")
+        outs.append(t)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = fa_bwd if q.dtype == torch.bfloat16 else fa_bwd_fp16
+    with torch.cuda.device(q.device):
+        st = fn(q, k, v, o, lse, dout, *outs, B, H, N, d, scale, causal, stream)
+    if st != FA_OK:
+        raise FAError(st, fn.__name__)
+    return tuple(outs)

@@ -2,7 +2,7 @@
 
     python -m io_aware_exact_fa2_amd.build
 
-compiles csrc/fa_fwd.hip into io_aware_exact_fa2_amd/libfa.so. Packed fp32 VALU
+compiles csrc/fa_fwd.hip and csrc/fa_bwd.hip into io_aware_exact_fa2_amd/libfa.so. Packed fp32 VALU
 forms are disabled for all device code (-packed-fp32-ops), and MFMA builtins use
 their VGPR-accumulator form.
 """
@@ -15,7 +15,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip")]
 OUT = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
@@ -42,7 +42,7 @@ def build_library(extra_flags=(), out: str = OUT, verbose: bool = False) -> str:
     """Compile the C-ABI library; returns its path. Always recompiles."""
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
-           SRC, "-o", tmp]
+           *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature; that warning is harmless
     msgs = [l for l in (res.stdout + res.stderr).splitlines()

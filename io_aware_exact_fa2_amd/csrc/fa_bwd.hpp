@@ -1,0 +1,318 @@
+// fa_bwd.hpp — backward pass of the attention forward in fa_fwd_*.hpp, for gfx950.
+//
+// What the pages fix ([P1] currybab.bearblog.dev, FA2 section, the LSE identity; [P2]
+// iq-universe.github.io, "FlashAttention: SRAM tiling으로 O(N²) HBM을 우회하다", the
+// activation-memory paragraph; [P3] ariser.io, "계산을 다시 하는 편이 싸다는 역설"): the
+// forward keeps only O and the per-row logsumexp L, and the backward recomputes the
+// probabilities block by block, P_ij = exp(S_ij - L_i), instead of storing the N x N
+// matrix. The gradients are the chain rule of the forward definition (for the loss
+// sum(O * dO)):
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = rowsum(dO * O)_i,
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// Two kernels, so that every output is written by exactly one workgroup (no atomics and
+// no workspace beyond the outputs):
+//   * fa_bwd_dq_kernel: one workgroup per 128 query rows (32 per wave) walks the key
+//     tiles, recomputing S^T and dP^T with the row on the lane (as in the forward), and
+//     accumulates dQ^T = K^T dS^T;
+//   * fa_bwd_dkdv_kernel: one workgroup per 128 keys (32 per wave) walks the query
+//     tiles, recomputing S and dP with the key on the lane, and accumulates
+//     dV^T = dO^T P and dK^T = Q^T dS.
+// D is recomputed from dO and O where it is needed. All products run on
+// v_mfma_f32_32x32x16_{bf16,f16}; an accumulator becomes a 16-bit B operand of the next
+// product by the row permutation of the forward kernels (bits 2 and 3 of the MFMA row
+// swapped). Tiles are staged in LDS with the forward's K swizzle; transposed operands
+// are read with ds_read_b64_tr_b16.
+#pragma once
+
+#include "fa_common.hpp"
+
+namespace fa {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int N;
+  int BH;
+  float scale;  // signed
+  float c;      // scale * log2(e), signed
+};
+
+// Stage rows [r0, r0 + ROWS) of a [N, D] matrix into LDS (swizzled 16-byte chunks; rows
+// at or past N as zeros), with all threads of the workgroup.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void bwd_stage(u32x4_t* lds, const uint16_t* src, int r0, int N,
+                                          int tid) {
+  constexpr int CPR = D / 8;
+  static_assert((ROWS * CPR) % NT == 0, "whole chunks per thread");
+#pragma unroll
+  for (int t = 0; t < ROWS * CPR / NT; ++t) {
+    const int idx = tid + NT * t, row = idx / CPR, ch = idx % CPR;
+    u32x4_t x = {0u, 0u, 0u, 0u};
+    if (r0 + row < N) x = ld16(src + (size_t)(r0 + row) * D + ch * 8);
+    lds[row * CPR + (ch ^ swz_k<D>(row))] = x;
+  }
+}
+
+// Per-lane byte offsets of the transposed operand reads (A = M^T over 16 rows of a
+// staged tile, one 32-column block db): half h covers rows 4h .. 4h+3 of each 8-row
+// group. The chunk swizzle depends on the row modulo 16 (D = 128) or on row / 2
+// modulo 8 (D = 64), which a multiple of 16 rows does not change: one offset per
+// (db, h), the 16-row step is a constant.
+template <int D>
+__device__ __forceinline__ uint32_t bwd_tr_off(int lane, int db, int h) {
+  constexpr int CPR = D / 8;
+  const int g16 = lane >> 4, t4 = (lane & 15) >> 2, u4 = lane & 3;
+  const int row = (g16 >> 1) * 8 + t4 + 4 * h;
+  const int ch = (4 * db + 2 * (g16 & 1) + (u4 >> 1)) ^ swz_k<D>(row);
+  return (uint32_t)((row * CPR + ch) * 16 + (u4 & 1) * 8);
+}
+
+// Transposed operand of a staged tile: columns 32 db .. 32 db + 31, rows 16 st .. +15.
+template <int D>
+__device__ __forceinline__ u32x4_t bwd_tr_frag(const u32x4_t* tile, const uint32_t (&off)[D / 32][2],
+                                               int db, int st) {
+  constexpr int CPR = D / 8;
+  const uint32_t b = (uint32_t)(uintptr_t)tile + 16 * st * CPR * 16;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(b + off[db][0]));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(b + off[db][1]));
+  const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+}
+
+// Row operand of a staged tile (A = M over 32 rows, 16 columns): MFMA row m reads tile
+// row r0 + key_of_row(m), columns 16 ds + 8 hh .. +7.
+template <int D>
+__device__ __forceinline__ u32x4_t bwd_row_frag(const u32x4_t* tile, int r0, int l32, int hh, int ds) {
+  constexpr int CPR = D / 8;
+  const int row = r0 + key_of_row(l32);
+  return tile[row * CPR + ((2 * ds + hh) ^ swz_k<D>(row))];
+}
+
+// Store a transposed accumulator set (rows = head dims, lane = one output row `row`)
+// times `mul` as 16-bit values into row `row` of a [N, D] matrix.
+template <bool BF16, int D>
+__device__ __forceinline__ void bwd_store_rows(uint16_t* dst, const f32x16_t (&acc)[D / 32], int row,
+                                               int hh, float mul) {
+  using E = Elt<BF16>;
+  uint16_t* r = dst + (size_t)row * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dcol = db * 32 + g * 8 + hh * 4;
+      const uint32_t w0 = E::pack(acc[db][4 * g + 0] * mul, acc[db][4 * g + 1] * mul);
+      const uint32_t w1 = E::pack(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
+      *reinterpret_cast<u32x2_t*>(r + dcol) = u32x2_t{w0, w1};
+    }
+}
+
+// ---- dQ: one workgroup per 128 query rows -------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
+  using E = Elt<BF16>;
+  constexpr int NW = 4, BQ = 128, BK = 64, CPR = D / 8, NDS = D / 16;
+  __shared__ __attribute__((aligned(1024))) u32x4_t ks[BK * CPR];
+  __shared__ __attribute__((aligned(1024))) u32x4_t vs[BK * CPR];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int N = p.N;
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int bh = blockIdx.x / n_qt;
+  const int qt = CAUSAL ? n_qt - 1 - blockIdx.x % n_qt : blockIdx.x % n_qt;  // long rows first
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const int q0 = qt * BQ, qi = q0 + wid * 32 + l32;
+  const int qr = min(qi, N - 1);  // rows past N load row N-1 and are never stored
+  const int n_kt = CAUSAL ? (min(q0 + BQ, N) + BK - 1) / BK : (N + BK - 1) / BK;
+  const bool wave_live = q0 + wid * 32 < N;
+  const int w_last = min(q0 + wid * 32 + 31, N - 1);
+
+  // Q and dO as B operands (lane: query qi, columns 16 ds + 8 hh .. +7), D_i and L_i
+  u32x4_t qf[NDS], dof[NDS];
+  float dpart = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    const size_t off = head + (size_t)qr * D + ds * 16 + hh * 8;
+    qf[ds] = ld16(p.q + off);
+    dof[ds] = ld16(p.dout + off);
+    const u32x4_t of = ld16(p.o + off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dpart = E::dot2(dof[ds][w], of[w], dpart);
+    }
+  }
+  const float Dq = xhalf_sum(dpart);
+  const float L2 = p.lse[(size_t)bh * N + qr] * 1.4426950408889634f;
+
+  f32x16_t dq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+  uint32_t troff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) troff[db][h] = bwd_tr_off<D>(lane, db, h);
+
+  for (int j = 0; j < n_kt; ++j) {
+    const int k0 = j * BK;
+    __syncthreads();  // the previous tile's reads are done
+    bwd_stage<D, BK, NW * 64>(ks, p.k + head, k0, N, tid);
+    bwd_stage<D, BK, NW * 64>(vs, p.v + head, k0, N, tid);
+    __syncthreads();
+    if (!wave_live || (CAUSAL && k0 > w_last)) continue;
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb) {
+      // S^T and dP^T of 32 keys x this wave's 32 queries
+      f32x16_t st = {}, dpt = {};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        st = E::mfma(bwd_row_frag<D>(ks, 32 * kb, l32, hh, ds), qf[ds], st);
+        dpt = E::mfma(bwd_row_frag<D>(vs, 32 * kb, l32, hh, ds), dof[ds], dpt);
+      }
+      // dS^T = P^T * (dP^T - D), P recomputed from L; masked entries are 0
+      u32x4_t dsop[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float v2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int key = k0 + 32 * kb + key_of_reg(r + e, hh);
+          const bool ok = key < N && (!CAUSAL || key <= qi);
+          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + e], p.c, -L2)) : 0.f;
+          v2[e] = pr * (dpt[r + e] - Dq);
+        }
+        dsop[r / 8][(r % 8) / 2] = E::pack(v2[0], v2[1]);
+      }
+      // dQ^T += K^T dS^T over these 32 keys (two 16-key steps)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dq[db] = E::mfma(bwd_tr_frag<D>(ks, troff, db, 2 * kb + s2), dsop[s2], dq[db]);
+    }
+  }
+  if (wave_live && qi < N) bwd_store_rows<BF16, D>(p.dq + head, dq, qi, hh, p.scale);
+}
+
+// ---- dK, dV: one workgroup per 128 keys ----------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
+  using E = Elt<BF16>;
+  constexpr int NW = 4, BKV = 128, BQ = 64, CPR = D / 8, NDS = D / 16;
+  __shared__ __attribute__((aligned(1024))) u32x4_t qs[BQ * CPR];
+  __shared__ __attribute__((aligned(1024))) u32x4_t dos[BQ * CPR];
+  __shared__ float lsh[BQ], dsh[BQ];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  const int N = p.N;
+  const int n_kt = (N + BKV - 1) / BKV;
+  const int bh = blockIdx.x / n_kt;
+  const int kt = blockIdx.x % n_kt;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const int k0 = kt * BKV, kj = k0 + wid * 32 + l32;
+  const bool wave_live = k0 + wid * 32 < N;
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int i0 = CAUSAL ? k0 / BQ : 0;  // queries before k0 never see these keys
+
+  // K and V of this wave's 32 keys as B operands (lane: key kj, columns 16 ds + 8 hh ..);
+  // keys past N load row N - 1 and are masked
+  u32x4_t kf[NDS], vf[NDS];
+  {
+    const int kr = min(kj, N - 1);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const size_t off = head + (size_t)kr * D + ds * 16 + hh * 8;
+      kf[ds] = ld16(p.k + off);
+      vf[ds] = ld16(p.v + off);
+    }
+  }
+
+  f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+  uint32_t troff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) troff[db][h] = bwd_tr_off<D>(lane, db, h);
+
+  for (int i = i0; i < n_qt; ++i) {
+    const int qb0 = i * BQ;
+    __syncthreads();  // the previous tile's reads are done
+    bwd_stage<D, BQ, NW * 64>(qs, p.q + head, qb0, N, tid);
+    bwd_stage<D, BQ, NW * 64>(dos, p.dout + head, qb0, N, tid);
+    {
+      // D and L of the tile's 64 rows: four lanes per row
+      const int row = tid >> 2, part = tid & 3, qrow = qb0 + row;
+      float acc = 0.f;
+      if (qrow < N) {
+        const uint16_t* dr = p.dout + head + (size_t)qrow * D + part * (D / 4);
+        const uint16_t* orow = p.o + head + (size_t)qrow * D + part * (D / 4);
+#pragma unroll
+        for (int c8 = 0; c8 < D / 32; ++c8) {
+          const u32x4_t a = ld16(dr + c8 * 8), b = ld16(orow + c8 * 8);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc = E::dot2(a[w], b[w], acc);
+        }
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (part == 0) {
+        dsh[row] = acc;
+        lsh[row] = qrow < N ? p.lse[(size_t)bh * N + qrow] * 1.4426950408889634f : 0.f;
+      }
+    }
+    __syncthreads();
+    if (!wave_live) continue;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      // S and dP of these 32 queries x this wave's 32 keys (row = query, lane = key)
+      f32x16_t s = {}, dp = {};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        s = E::mfma(bwd_row_frag<D>(qs, 32 * qb, l32, hh, ds), kf[ds], s);
+        dp = E::mfma(bwd_row_frag<D>(dos, 32 * qb, l32, hh, ds), vf[ds], dp);
+      }
+      u32x4_t pop[2], dsop[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float pv[2], dv2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int ql = 32 * qb + key_of_reg(r + e, hh), q = qb0 + ql;
+          const bool ok = q < N && kj < N && (!CAUSAL || kj <= q);
+          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + e], p.c, -lsh[ql])) : 0.f;
+          pv[e] = pr;
+          dv2[e] = pr * (dp[r + e] - dsh[ql]);
+        }
+        pop[r / 8][(r % 8) / 2] = E::pack(pv[0], pv[1]);
+        dsop[r / 8][(r % 8) / 2] = E::pack(dv2[0], dv2[1]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries (two 16-query steps)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = E::mfma(bwd_tr_frag<D>(dos, troff, db, 2 * qb + s2), pop[s2], dv[db]);
+          dk[db] = E::mfma(bwd_tr_frag<D>(qs, troff, db, 2 * qb + s2), dsop[s2], dk[db]);
+        }
+    }
+  }
+  if (wave_live && kj < N) {
+    bwd_store_rows<BF16, D>(p.dk + head, dk, kj, hh, p.scale);
+    bwd_store_rows<BF16, D>(p.dv + head, dv, kj, hh, 1.0f);
+  }
+}
+
+}  // namespace fa

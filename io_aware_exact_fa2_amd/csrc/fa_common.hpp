@@ -1,4 +1,4 @@
-// fa_common.hpp — types and helpers shared by the attention forward kernels (gfx950).
+// fa_common.hpp — types and helpers shared by the attention kernels (gfx950).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,6 +49,11 @@ template <> struct Elt<true> {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
                                            __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
   }
+  // acc + a.lo * b.lo + a.hi * b.hi of two packed pairs
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+  }
 };
 template <> struct Elt<false> {
   static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -64,6 +69,11 @@ template <> struct Elt<false> {
   static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w),
                                   __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
+  }
+  // acc + a.lo * b.lo + a.hi * b.hi of two packed pairs
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
   }
 };
 

@@ -4,17 +4,19 @@
 #include "fa_fwd_fast.hpp"
 #include "fa_fwd_generic.hpp"
 #include "fa_fwd_wide.hpp"
+#include "fa_host.hpp"
 
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <mutex>
 
 namespace {
 
-thread_local int g_last_hip_error = 0;
+using fa_host::cu_count;
+using fa_host::g_last_hip_error;
+using fa_host::ranges_overlap;
 
 // Launch shapes. The fast path (d = 64, 128) is tunable at build time for sweeps;
 // the defaults are the measured best. The generic path (other d) is fixed.
@@ -55,26 +57,6 @@ constexpr int kQB = 1;                    //               32-query blocks per w
 constexpr int kBC = 64;                   //               keys per tile
 constexpr int kGBR = kNW * kQB * 32;      //               queries per workgroup
 constexpr int kMinBR = kFNW * 32 < kGBR ? kFNW * 32 : kGBR;   // smallest query tile
-
-// CU count of the current device, read once per device (immutable afterwards).
-int cu_count() {
-  static std::once_flag once[64];
-  static int count[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  std::call_once(once[dev], [dev]() {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    count[dev] = n;
-  });
-  return count[dev];
-}
-
-bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
-  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
-  const uintptr_t b0 = reinterpret_cast<uintptr_t>(b);
-  return a0 < b0 + nb && b0 < a0 + na;
-}
 
 int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
              int B, int H, int N, int d, float scale, float tau) {

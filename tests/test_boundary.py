@@ -125,6 +125,42 @@ def test_fa_fwd_ex_validation(L, no_gpu):
     assert fa.fa_last_hip_error() == 0
 
 
+# fake addresses of the backward's extra buffers (same spacing as above)
+DOA, DQA, DKA, DVA = (0x7f0000000000 + i * 0x100000000 for i in range(5, 9))
+
+
+@pytest.mark.parametrize("fn", [fa.fa_bwd, fa.fa_bwd_fp16])
+def test_backward_validation_errors(L, no_gpu, fn):
+    def call(q=QA, k=KA, v=VA, o=OA, lse=LA, do=DOA, dq=DQA, dk=DKA, dv=DVA, **kw):
+        a = dict(GOOD, **kw)
+        return fn(q, k, v, o, lse, do, dq, dk, dv, a["B"], a["H"], a["N"], a["d"],
+                  a["scale"], a["causal"], None)
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert call(**{name: 0}) == fa.FA_ERR_NULL, name
+    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(d=0), dict(N=-5)):
+        assert call(**bad) == fa.FA_ERR_SHAPE, bad
+    for s in (float("nan"), float("inf")):
+        assert call(scale=s) == fa.FA_ERR_SHAPE
+    for d in (1, 32, 63, 65, 96, 127, 129):
+        assert call(d=d) == fa.FA_ERR_UNSUPPORTED, d
+    assert call(N=2 ** 24, d=128) == fa.FA_ERR_SHAPE
+    assert call(B=2 ** 20, H=2 ** 10, N=1024) == fa.FA_ERR_SHAPE
+    for name in ("q", "do", "dq", "dk", "dv"):
+        assert call(**{name: DQA + 0x40000008}) == fa.FA_ERR_ALIGN, name
+    assert call(lse=LA + 2) == fa.FA_ERR_ALIGN
+    tbytes = GOOD["B"] * GOOD["H"] * GOOD["N"] * GOOD["d"] * 2
+    # outputs overlapping an input or each other
+    assert call(dq=QA) == fa.FA_ERR_ALIAS
+    assert call(dk=OA + 16 * ((tbytes - 16) // 16)) == fa.FA_ERR_ALIAS
+    assert call(dv=DOA) == fa.FA_ERR_ALIAS
+    assert call(dv=LA - 16 * ((tbytes - 16) // 16)) == fa.FA_ERR_ALIAS
+    assert call(dk=DQA) == fa.FA_ERR_ALIAS
+    assert call(dv=DKA + 16) == fa.FA_ERR_ALIAS
+    # inputs may alias each other
+    assert call(k=QA, v=QA, dq=QA) == fa.FA_ERR_ALIAS
+    assert fa.fa_last_hip_error() == 0
+
+
 def test_inputs_may_alias_each_other(L, no_gpu):
     """q, k, v are read-only and may share memory; that is not an alias error.
     Checked through validation only: with o aliasing q the call must still

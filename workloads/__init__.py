@@ -26,7 +26,9 @@ Workloads (shapes are [B, H, N, d], row-major, contiguous):
                 N is not a multiple of any tile size.
 
 Draw order inside one call: Q, K, V, then the spike row indices (one
-``choice`` per head, heads in (b, h) order), then the spike directions.
+``choice`` per head, heads in (b, h) order), then the spike directions. The
+output gradient dO of the backward pass is drawn by ``make_grad`` from a
+separate stream, N(0, 1) for every workload.
 """
 from __future__ import annotations
 
@@ -36,7 +38,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "to_f64", "scaled"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_grad", "to_f64", "scaled"]
 
 
 @dataclass(frozen=True)
@@ -118,6 +120,14 @@ def make_inputs(w: Workload, seed: int | None = None):
         raise ValueError(f"unknown distribution {w.dist!r}")
     dt = w.torch_dtype
     return _round(q, dt), _round(k, dt), _round(v, dt)
+
+
+def make_grad(w: Workload, seed: int | None = None) -> torch.Tensor:
+    """dO for the backward pass: [B, H, N, d] ~ N(0, 1), rounded to the workload's dtype,
+    from its own stream (seed + 10007 unless given), so Q, K, V are unchanged."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + 10007 if seed is None else seed))
+    g = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
+    return _round(g, w.torch_dtype)
 
 
 def spike_rows(w: Workload, seed: int | None = None):
