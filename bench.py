@@ -50,7 +50,9 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, steps, warmup):
+def _launcher(w, leg="fwd"):
+    """(fn, args) of one launch of the forward ("fwd") or backward ("bwd") pass on
+    seeded inputs of workload w, resident on cuda:0."""
     import torch
     import io_aware_exact_fa2_amd as fa
     import workloads
@@ -61,6 +63,24 @@ def time_gpu(w, steps, warmup):
     stream = torch.cuda.current_stream()
     fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_fp16
     args = (q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream)
+    if leg == "fwd":
+        return fn, args
+    st = fn(*args)
+    if st != fa.FA_OK:
+        raise fa.FAError(st)
+    do = workloads.make_grad(w).to("cuda:0")
+    grads = [torch.empty_like(q) for _ in range(3)]
+    fn = fa.fa_bwd if w.dtype == "bf16" else fa.fa_bwd_fp16
+    return fn, (q, k, v, o, lse, do, *grads, w.B, w.H, w.N, w.d, w.scale, int(w.causal),
+                stream)
+
+
+def time_gpu(w, steps, warmup, leg="fwd"):
+    import torch
+    import io_aware_exact_fa2_amd as fa
+
+    fn, args = _launcher(w, leg)
+    stream = args[-1]
     for _ in range(warmup):
         st = fn(*args)
         if st != fa.FA_OK:
@@ -238,6 +258,8 @@ def main(argv=None):
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--also", default="causal8k,long32k,stress4000",
                     help="extra workloads timed for the 'workloads' field ('' for none)")
+    ap.add_argument("--backward", default="ai2048,causal8k,long32k,stress4000",
+                    help="workloads whose backward pass is also timed (comma list; empty: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-hbm", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -281,6 +303,15 @@ def main(argv=None):
         extra[name] = {"ms": round(msx, 4), "tflops": round(tx, 1),
                        "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1), "dtype": wx.dtype,
                        "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d]}
+    bwd = {}
+    for name in [s for s in a.backward.split(",") if s]:
+        wx = workloads.get(name)
+        msx, _, _ = time_gpu(wx, max(5, a.steps // 5), 3, leg="bwd")
+        tx = 2.5 * wx.flops() / (msx * 1e-3) / 1e12
+        bwd[name] = {"ms": round(msx, 4), "tflops": round(tx, 1),
+                     "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1), "dtype": wx.dtype,
+                     "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d],
+                     "flops": "2.5 x forward: five N x N x d products (dV, dP, dQ, dK, S)"}
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -306,6 +337,7 @@ def main(argv=None):
         "roofline": roof,
         "cold": cold,
         "workloads": extra,
+        "backward": bwd,
     }
     if a.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)

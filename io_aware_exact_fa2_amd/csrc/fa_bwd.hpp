@@ -20,8 +20,9 @@
 // D is recomputed from dO and O where it is needed. All products run on
 // v_mfma_f32_32x32x16_{bf16,f16}; an accumulator becomes a 16-bit B operand of the next
 // product by the row permutation of the forward kernels (bits 2 and 3 of the MFMA row
-// swapped). Tiles are staged in LDS with the forward's K swizzle; transposed operands
-// are read with ds_read_b64_tr_b16.
+// swapped). Tiles are staged in LDS through registers (the next tile's loads are in
+// flight while the current one is computed) with a swizzle that keeps both the row
+// reads and the transposed reads (ds_read_b64_tr_b16) free of bank conflicts.
 #pragma once
 
 #include "fa_common.hpp"
@@ -44,33 +45,80 @@ struct BwdParams {
   float c;      // scale * log2(e), signed
 };
 
-// Stage rows [r0, r0 + ROWS) of a [N, D] matrix into LDS (swizzled 16-byte chunks; rows
-// at or past N as zeros), with all threads of the workgroup.
+// XOR swizzle of the 16-byte chunks of LDS row `row` of a staged tile. The tiles are
+// read two ways: as MFMA row operands (16 lanes read one logical chunk of 16
+// consecutive rows) and transposed with ds_read_b64_tr_b16 (a half-wave reads 4
+// consecutive rows x 4 consecutive chunks). Both are bank-conflict free when the
+// swizzle is a bijection of the rows within a 256-byte bank line (d = 128: rows
+// 0..15; d = 64: the 8 rows of each parity) whose bits 2..3 differ between any two of
+// 4 consecutive rows of one parity class.
+template <int D> __device__ __forceinline__ int swz_b(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+
+// Rows [r0, r0 + ROWS) of a [N, D] matrix held in registers on their way to LDS: all
+// threads of the workgroup load whole 16-byte chunks (rows at or past N as zeros), so
+// the next tile's loads can be in flight while the current tile is computed.
 template <int D, int ROWS, int NT>
-__device__ __forceinline__ void bwd_stage(u32x4_t* lds, const uint16_t* src, int r0, int N,
-                                          int tid) {
-  constexpr int CPR = D / 8;
+struct BwdTile {
+  static constexpr int CPR = D / 8, PER = ROWS * CPR / NT;
   static_assert((ROWS * CPR) % NT == 0, "whole chunks per thread");
+  u32x4_t x[PER];
+  // chunk t of this thread: row tid / CPR + t * NT / CPR, chunk tid % CPR
+  static __device__ __forceinline__ int row_of(int tid, int t) { return (tid + NT * t) / CPR; }
+  __device__ __forceinline__ void load(const uint16_t* src, int r0, int N, int tid) {
 #pragma unroll
-  for (int t = 0; t < ROWS * CPR / NT; ++t) {
-    const int idx = tid + NT * t, row = idx / CPR, ch = idx % CPR;
-    u32x4_t x = {0u, 0u, 0u, 0u};
-    if (r0 + row < N) x = ld16(src + (size_t)(r0 + row) * D + ch * 8);
-    lds[row * CPR + (ch ^ swz_k<D>(row))] = x;
+    for (int t = 0; t < PER; ++t) {
+      const int row = row_of(tid, t), ch = tid % CPR;
+      x[t] = u32x4_t{0u, 0u, 0u, 0u};
+      if (r0 + row < N) x[t] = ld16(src + (size_t)(r0 + row) * D + ch * 8);
+    }
+  }
+  __device__ __forceinline__ void store(u32x4_t* lds, int tid) const {
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int row = row_of(tid, t), ch = tid % CPR;
+      lds[row * CPR + (ch ^ swz_b<D>(row))] = x[t];
+    }
+  }
+};
+
+// Workgroup -> (head, tile rank). When B*H is a multiple of 8 the tiles of one head
+// stay on one XCD (workgroups are dispatched round-robin over the 8 XCDs), so its
+// rows are fetched into one L2 only. Under the causal mask rank 0 is the tile with the
+// most work and ranks are issued in increasing order over all heads, so the short
+// tiles fill the tail of the grid.
+template <bool CAUSAL>
+__device__ __forceinline__ void bwd_decode(int bid, int BH, int n_t, int& bh, int& rank) {
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, s = bid >> 3, hpx = BH >> 3;
+    if (CAUSAL) {
+      rank = s / hpx;
+      bh = (s % hpx) * 8 + xcd;
+    } else {
+      bh = xcd * hpx + s / n_t;
+      rank = s % n_t;
+    }
+  } else if (CAUSAL) {
+    rank = bid / BH;
+    bh = bid % BH;
+  } else {
+    bh = bid / n_t;
+    rank = bid % n_t;
   }
 }
 
 // Per-lane byte offsets of the transposed operand reads (A = M^T over 16 rows of a
 // staged tile, one 32-column block db): half h covers rows 4h .. 4h+3 of each 8-row
-// group. The chunk swizzle depends on the row modulo 16 (D = 128) or on row / 2
-// modulo 8 (D = 64), which a multiple of 16 rows does not change: one offset per
-// (db, h), the 16-row step is a constant.
+// group. The chunk swizzle depends on the row modulo 16 only, which a multiple of
+// 16 rows does not change: one offset per (db, h), the 16-row step is a constant.
 template <int D>
 __device__ __forceinline__ uint32_t bwd_tr_off(int lane, int db, int h) {
   constexpr int CPR = D / 8;
   const int g16 = lane >> 4, t4 = (lane & 15) >> 2, u4 = lane & 3;
   const int row = (g16 >> 1) * 8 + t4 + 4 * h;
-  const int ch = (4 * db + 2 * (g16 & 1) + (u4 >> 1)) ^ swz_k<D>(row);
+  const int ch = (4 * db + 2 * (g16 & 1) + (u4 >> 1)) ^ swz_b<D>(row);
   return (uint32_t)((row * CPR + ch) * 16 + (u4 & 1) * 8);
 }
 
@@ -92,7 +140,7 @@ template <int D>
 __device__ __forceinline__ u32x4_t bwd_row_frag(const u32x4_t* tile, int r0, int l32, int hh, int ds) {
   constexpr int CPR = D / 8;
   const int row = r0 + key_of_row(l32);
-  return tile[row * CPR + ((2 * ds + hh) ^ swz_k<D>(row))];
+  return tile[row * CPR + ((2 * ds + hh) ^ swz_b<D>(row))];
 }
 
 // Store a transposed accumulator set (rows = head dims, lane = one output row `row`)
@@ -123,8 +171,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int N = p.N;
   const int n_qt = (N + BQ - 1) / BQ;
-  const int bh = blockIdx.x / n_qt;
-  const int qt = CAUSAL ? n_qt - 1 - blockIdx.x % n_qt : blockIdx.x % n_qt;  // long rows first
+  int bh, rank;
+  bwd_decode<CAUSAL>(blockIdx.x, p.BH, n_qt, bh, rank);
+  const int qt = CAUSAL ? n_qt - 1 - rank : rank;  // the last query tile sees the most keys
   const size_t head = (size_t)bh * (size_t)N * D;
   const int q0 = qt * BQ, qi = q0 + wid * 32 + l32;
   const int qr = min(qi, N - 1);  // rows past N load row N-1 and are never stored
@@ -160,12 +209,19 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) troff[db][h] = bwd_tr_off<D>(lane, db, h);
 
+  BwdTile<D, BK, NW * 64> kt_next, vt_next;
+  kt_next.load(p.k + head, 0, N, tid);
+  vt_next.load(p.v + head, 0, N, tid);
   for (int j = 0; j < n_kt; ++j) {
     const int k0 = j * BK;
     __syncthreads();  // the previous tile's reads are done
-    bwd_stage<D, BK, NW * 64>(ks, p.k + head, k0, N, tid);
-    bwd_stage<D, BK, NW * 64>(vs, p.v + head, k0, N, tid);
+    kt_next.store(ks, tid);
+    vt_next.store(vs, tid);
     __syncthreads();
+    if (j + 1 < n_kt) {  // in flight while this tile is computed
+      kt_next.load(p.k + head, k0 + BK, N, tid);
+      vt_next.load(p.v + head, k0 + BK, N, tid);
+    }
     if (!wave_live || (CAUSAL && k0 > w_last)) continue;
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
@@ -212,8 +268,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int N = p.N;
   const int n_kt = (N + BKV - 1) / BKV;
-  const int bh = blockIdx.x / n_kt;
-  const int kt = blockIdx.x % n_kt;
+  int bh, kt;
+  bwd_decode<CAUSAL>(blockIdx.x, p.BH, n_kt, bh, kt);  // the first key tile sees the most queries
   const size_t head = (size_t)bh * (size_t)N * D;
   const int k0 = kt * BKV, kj = k0 + wid * 32 + l32;
   const bool wave_live = k0 + wid * 32 < N;
@@ -247,33 +303,43 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) troff[db][h] = bwd_tr_off<D>(lane, db, h);
 
+  // Q, dO and O of the next query tile, and its L, in flight while a tile is computed
+  using Tile = BwdTile<D, BQ, NW * 64>;
+  Tile qn, don, on;
+  float ln[Tile::PER];
+  auto fetch = [&](int qb0) {
+    qn.load(p.q + head, qb0, N, tid);
+    don.load(p.dout + head, qb0, N, tid);
+    on.load(p.o + head, qb0, N, tid);
+#pragma unroll
+    for (int t = 0; t < Tile::PER; ++t) {
+      const int q = qb0 + Tile::row_of(tid, t);
+      ln[t] = q < N ? p.lse[(size_t)bh * N + q] : 0.f;
+    }
+  };
+  fetch(i0 * BQ);
   for (int i = i0; i < n_qt; ++i) {
     const int qb0 = i * BQ;
     __syncthreads();  // the previous tile's reads are done
-    bwd_stage<D, BQ, NW * 64>(qs, p.q + head, qb0, N, tid);
-    bwd_stage<D, BQ, NW * 64>(dos, p.dout + head, qb0, N, tid);
-    {
-      // D and L of the tile's 64 rows: four lanes per row
-      const int row = tid >> 2, part = tid & 3, qrow = qb0 + row;
+    qn.store(qs, tid);
+    don.store(dos, tid);
+    // D_i = rowsum(dO * O) and L_i of the tile's rows: the CPR threads holding one row
+    // (consecutive lanes) reduce their chunks' dot products
+#pragma unroll
+    for (int t = 0; t < Tile::PER; ++t) {
       float acc = 0.f;
-      if (qrow < N) {
-        const uint16_t* dr = p.dout + head + (size_t)qrow * D + part * (D / 4);
-        const uint16_t* orow = p.o + head + (size_t)qrow * D + part * (D / 4);
 #pragma unroll
-        for (int c8 = 0; c8 < D / 32; ++c8) {
-          const u32x4_t a = ld16(dr + c8 * 8), b = ld16(orow + c8 * 8);
+      for (int w = 0; w < 4; ++w) acc = E::dot2(don.x[t][w], on.x[t][w], acc);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) acc = E::dot2(a[w], b[w], acc);
-        }
-      }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (part == 0) {
+      for (int m = 1; m < CPR; m <<= 1) acc += __shfl_xor(acc, m);
+      if (tid % CPR == 0) {
+        const int row = Tile::row_of(tid, t);
         dsh[row] = acc;
-        lsh[row] = qrow < N ? p.lse[(size_t)bh * N + qrow] * 1.4426950408889634f : 0.f;
+        lsh[row] = ln[t] * 1.4426950408889634f;
       }
     }
     __syncthreads();
+    if (i + 1 < n_qt) fetch(qb0 + BQ);
     if (!wave_live) continue;
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
