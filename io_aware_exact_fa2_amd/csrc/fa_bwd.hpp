@@ -29,6 +29,8 @@
 
 namespace fa {
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -180,6 +182,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
   const int n_kt = CAUSAL ? (min(q0 + BQ, N) + BK - 1) / BK : (N + BK - 1) / BK;
   const bool wave_live = q0 + wid * 32 < N;
   const int w_last = min(q0 + wid * 32 + 31, N - 1);
+  const int lim = CAUSAL ? min(qi, N - 1) : N - 1;  // last key this lane's query sees
 
   // Q and dO as B operands (lane: query qi, columns 16 ds + 8 hh .. +7), D_i and L_i
   u32x4_t qf[NDS], dof[NDS];
@@ -232,16 +235,17 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
         st = E::mfma(bwd_row_frag<D>(ks, 32 * kb, l32, hh, ds), qf[ds], st);
         dpt = E::mfma(bwd_row_frag<D>(vs, 32 * kb, l32, hh, ds), dof[ds], dpt);
       }
-      // dS^T = P^T * (dP^T - D), P recomputed from L; masked entries are 0
+      // dS^T = P^T * (dP^T - D), P recomputed from L; register r holds key
+      // k0 + 32 kb + 8 hh + rc(r), allowed when rc(r) <= t
+      const int t = lim - (k0 + 32 * kb + 8 * hh);
       u32x4_t dsop[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float v2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int key = k0 + 32 * kb + key_of_reg(r + e, hh);
-          const bool ok = key < N && (!CAUSAL || key <= qi);
-          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + e], p.c, -L2)) : 0.f;
+          const int rc = key_of_reg(r + e, 0);
+          const float pr = rc <= t ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + e], p.c, -L2)) : 0.f;
           v2[e] = pr * (dpt[r + e] - Dq);
         }
         dsop[r / 8][(r % 8) / 2] = E::pack(v2[0], v2[1]);
@@ -264,7 +268,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
   constexpr int NW = 4, BKV = 128, BQ = 64, CPR = D / 8, NDS = D / 16;
   __shared__ __attribute__((aligned(1024))) u32x4_t qs[BQ * CPR];
   __shared__ __attribute__((aligned(1024))) u32x4_t dos[BQ * CPR];
-  __shared__ float lsh[BQ], dsh[BQ];
+  __shared__ __attribute__((aligned(16))) float lsh[BQ];
+  __shared__ __attribute__((aligned(16))) float dsh[BQ];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int N = p.N;
   const int n_kt = (N + BKV - 1) / BKV;
@@ -350,17 +355,30 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
         s = E::mfma(bwd_row_frag<D>(qs, 32 * qb, l32, hh, ds), kf[ds], s);
         dp = E::mfma(bwd_row_frag<D>(dos, 32 * qb, l32, hh, ds), vf[ds], dp);
       }
+      // L and D of the rows: register r holds query qb0 + 32 qb + 8 hh + rc(r), with
+      // rc(r) = (r & 7) + 16 (r >> 3); it sees this lane's key when lo <= rc(r) < hi
+      f32x4_t lv[4], dv4[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * qb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+        lv[g] = *reinterpret_cast<const f32x4_t*>(lsh + ql);
+        dv4[g] = *reinterpret_cast<const f32x4_t*>(dsh + ql);
+      }
+      const int base = qb0 + 32 * qb + 8 * hh;
+      const int lo = CAUSAL ? kj - base : -32;
+      const int hi = kj < N ? N - base : -32;
       u32x4_t pop[2], dsop[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float pv[2], dv2[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int ql = 32 * qb + key_of_reg(r + e, hh), q = qb0 + ql;
-          const bool ok = q < N && kj < N && (!CAUSAL || kj <= q);
-          const float pr = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + e], p.c, -lsh[ql])) : 0.f;
+          const int re = r + e, rc = key_of_reg(re, 0);
+          const float pr = (rc >= lo && rc < hi)
+                               ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[re], p.c, -lv[re / 4][re % 4]))
+                               : 0.f;
           pv[e] = pr;
-          dv2[e] = pr * (dp[r + e] - dsh[ql]);
+          dv2[e] = pr * (dp[re] - dv4[re / 4][re % 4]);
         }
         pop[r / 8][(r % 8) / 2] = E::pack(pv[0], pv[1]);
         dsop[r / 8][(r % 8) / 2] = E::pack(dv2[0], dv2[1]);
