@@ -22,6 +22,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -44,6 +46,9 @@ enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
  * (log2 units; see fa_fwd_ex). */
 #define FA_DEFAULT_RESCALE_LOG2 8.0f
 #define FA_MAX_RESCALE_LOG2 15.0f
+
+/* Largest split count fa_fwd_splitkv accepts. */
+#define FA_MAX_SPLITS 64
 
 /*
  * fa_fwd — exact attention forward in the FA2 loop order, bfloat16 tensors.
@@ -128,6 +133,60 @@ int fa_fwd_fp16(const void* q, const void* k, const void* v, void* o, float* lse
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int N, int d, float scale, int causal, int dtype,
               float rescale_log2, void* stream);
+
+/*
+ * fa_fwd_splitkv — the operation of fa_fwd_ex (same outputs, up to rounding), with the
+ * keys of every head split into ranges that separate workgroups process, for shapes
+ * whose B * H * ceil(N / 256) query tiles are too few to fill the GPU (few heads,
+ * moderate N).
+ *
+ * Each split runs the FA2-order forward over its key range and leaves its normalized
+ * partial output O_s and partial logsumexp L_s (float32) in the workspace; a second
+ * kernel merges them per row as L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s,
+ * the block merge of the online softmax ([P1] "Online Softmax 개념"; [P3]
+ * "소프트맥스는 나누어 계산할 수 있다", the [1,2,3,4] example split into two blocks
+ * of two).
+ *
+ * n_splits in [1, FA_MAX_SPLITS] is an upper bound: the keys per split are
+ * ceil(N / n_splits) rounded up to a multiple of 256, so fewer splits may run. Under
+ * the causal mask a split that lies wholly after a query tile contributes L_s = -inf.
+ * d must be 64 or 128 (FA_ERR_UNSUPPORTED) and scale nonzero (FA_ERR_SHAPE).
+ *
+ * workspace: device memory of at least fa_fwd_splitkv_workspace_size(B, H, N, d,
+ * n_splits) bytes, 256-byte aligned, overlapping no tensor argument; owned by the
+ * caller, contents on entry ignored and on return unspecified. Concurrent calls need
+ * distinct workspaces. Other arguments, ownership, errors and asynchrony as fa_fwd_ex
+ * (dtype FA_DTYPE_BF16 / FA_DTYPE_FP16; the rescale threshold is the default).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, int n_splits, int dtype, void* stream);
+
+/* Bytes of workspace fa_fwd_splitkv needs for these sizes; 0 when they are invalid
+ * (B, H, N < 1, d not 64 or 128, n_splits outside [1, FA_MAX_SPLITS]). Host only. */
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits);
+
+/*
+ * fa_fwd_fa1 — the same outputs as fa_fwd_ex (up to rounding), computed in the FA1
+ * loop order as an ablation of the FA2 order of fa_fwd ([P1] "FlashAttention 1
+ * forward pass 알고리즘 분석" and the "정리" table): one workgroup per (batch, head)
+ * walks the key/value blocks in the outer loop and all query blocks in the inner loop,
+ * merging each block into the running m_i, l_i and normalized O_i with the alpha/beta
+ * update and writing them back to device memory after every key block. Q is read
+ * T_c = ceil(N / 64) times and O_i round-trips through memory, which is what the
+ * table's HBM column counts; it is slow on purpose (B * H workgroups only).
+ *
+ * workspace: at least fa_fwd_fa1_workspace_size(B, H, N, d) bytes (float32 O_i, m_i,
+ * l_i), 256-byte aligned, overlapping no tensor argument; caller-owned, contents on
+ * entry ignored. d must be 64 or 128 and scale nonzero. Other arguments, errors and
+ * asynchrony as fa_fwd_ex.
+ */
+int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse,
+               void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+               float scale, int causal, int dtype, void* stream);
+
+/* Bytes of workspace fa_fwd_fa1 needs; 0 for invalid sizes. Host only. */
+size_t fa_fwd_fa1_workspace_size(int B, int H, int N, int d);
 
 /*
  * fa_bwd — gradients of the attention of fa_fwd with respect to q, k and v,

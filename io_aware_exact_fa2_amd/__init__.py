@@ -21,7 +21,8 @@ __all__ = [
     "FA_OK", "FA_ERR_NULL", "FA_ERR_SHAPE", "FA_ERR_UNSUPPORTED", "FA_ERR_ALIAS",
     "FA_ERR_ALIGN", "FA_ERR_HIP", "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError",
     "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
-    "fa_bwd", "fa_bwd_fp16", "backward",
+    "fa_bwd", "fa_bwd_fp16", "backward", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+    "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "forward_splitkv", "forward_fa1", "FA_MAX_SPLITS",
     "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
 ]
@@ -36,8 +37,10 @@ FA_ERR_HIP = -6
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
+EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
            "fa_strerror", "fa_last_hip_error", "fa_version")
+FA_MAX_SPLITS = 64
 FA_DEFAULT_RESCALE_LOG2 = 8.0
 FA_MAX_RESCALE_LOG2 = 15.0
 
@@ -76,6 +79,15 @@ def lib() -> ctypes.CDLL:
         fn.restype = i
     L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, vp]
     L.fa_fwd_ex.restype = i
+    sz = ctypes.c_size_t
+    L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, i, vp]
+    L.fa_fwd_splitkv.restype = i
+    L.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_fwd_splitkv_workspace_size.restype = sz
+    L.fa_fwd_fa1.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    L.fa_fwd_fa1.restype = i
+    L.fa_fwd_fa1_workspace_size.argtypes = [i, i, i, i]
+    L.fa_fwd_fa1_workspace_size.restype = sz
     for name in ("fa_bwd", "fa_bwd_fp16"):
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
@@ -124,6 +136,30 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, rescale_log2,
     return lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                            float(scale), int(causal), int(dtype), float(rescale_log2),
                            _stream(stream))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                   n_splits, dtype, stream=None) -> int:
+    """C ``fa_fwd_splitkv``: key ranges in separate workgroups, then an LSE merge."""
+    return lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                int(workspace_bytes), B, H, N, d, float(scale), int(causal),
+                                int(n_splits), int(dtype), _stream(stream))
+
+
+def fa_fwd_splitkv_workspace_size(B, H, N, d, n_splits) -> int:
+    return lib().fa_fwd_splitkv_workspace_size(B, H, N, d, n_splits)
+
+
+def fa_fwd_fa1(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal, dtype,
+               stream=None) -> int:
+    """C ``fa_fwd_fa1``: the FA1 loop order (ablation)."""
+    return lib().fa_fwd_fa1(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                            int(workspace_bytes), B, H, N, d, float(scale), int(causal),
+                            int(dtype), _stream(stream))
+
+
+def fa_fwd_fa1_workspace_size(B, H, N, d) -> int:
+    return lib().fa_fwd_fa1_workspace_size(B, H, N, d)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream=None) -> int:
@@ -242,3 +278,51 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
     if st != FA_OK:
         raise FAError(st, fn.__name__)
     return tuple(outs)
+
+
+def _workspace_call(name, size_fn, call_fn, q, k, v, causal, scale, stream, extra, workspace):
+    import torch
+
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("q, k, v must share dtype bfloat16 or float16")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have the same [B, H, N, d] shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = size_fn(B, H, N, d, *extra)
+    if need == 0:
+        raise FAError(FA_ERR_SHAPE if d in (64, 128) else FA_ERR_UNSUPPORTED, name)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dt = FA_DTYPE_BF16 if q.dtype == torch.bfloat16 else FA_DTYPE_FP16
+    with torch.cuda.device(q.device):
+        st = call_fn(q, k, v, out, lse, workspace, workspace.numel() * workspace.element_size(),
+                     B, H, N, d, scale, causal, *extra, dt, stream)
+    if st != FA_OK:
+        raise FAError(st, name)
+    return out, lse
+
+
+def forward_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                    n_splits: int = 4, stream=None, workspace=None):
+    """O, L by the split-KV path (``fa_fwd_splitkv``); d = 64 or 128. The workspace
+    (a uint8 CUDA tensor of at least ``fa_fwd_splitkv_workspace_size`` bytes) is
+    allocated here unless given."""
+    return _workspace_call("fa_fwd_splitkv", fa_fwd_splitkv_workspace_size, fa_fwd_splitkv,
+                           q, k, v, causal, scale, stream, (int(n_splits),), workspace)
+
+
+def forward_fa1(q, k, v, causal: bool = False, scale: float | None = None, stream=None,
+                workspace=None):
+    """O, L in the FA1 loop order (``fa_fwd_fa1``, an ablation); d = 64 or 128."""
+    return _workspace_call("fa_fwd_fa1", fa_fwd_fa1_workspace_size, fa_fwd_fa1,
+                           q, k, v, causal, scale, stream, (), workspace)

@@ -30,6 +30,11 @@ struct Params {
   int xcd_map;    // 1 when BH % 8 == 0: the heads of one XCD stay on it
   float tau;      // rescale threshold in log2 units (fast kernel; 0: every tile)
   int next_stride;  // > 0: workgroup b warms the L2 with the Q tile of workgroup b + next_stride
+  // split-KV partial pass: keys [s * split_keys, (s + 1) * split_keys) for split s; the
+  // normalized partial O (float32) and partial L of split s go to o_part / l_part
+  int split_keys;
+  float* o_part;
+  float* l_part;
 };
 
 // --- element type -----------------------------------------------------------------

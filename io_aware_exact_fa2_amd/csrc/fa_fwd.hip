@@ -1,7 +1,9 @@
 // fa_fwd.hip — host side of the C ABI declared in include/fa.h: argument
 // validation (entirely before any HIP call), kernel selection and launch.
 #include "fa.h"
+#include "fa_fwd_fa1.hpp"
 #include "fa_fwd_fast.hpp"
+#include "fa_fwd_split.hpp"
 #include "fa_fwd_generic.hpp"
 #include "fa_fwd_wide.hpp"
 #include "fa_host.hpp"
@@ -141,6 +143,9 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
   p.tau = tau;
   p.next_stride = 0;
+  p.split_keys = 0;
+  p.o_part = nullptr;
+  p.l_part = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t e;
@@ -165,9 +170,192 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   return FA_OK;
 }
 
+// ---- split-KV and FA1-order passes (caller-provided workspace) --------------------
+constexpr int kSplitBR = kFNW * 32;  // query rows per split-KV workgroup (fast kernel)
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Effective split count and keys per split (a multiple of the query tile), or 0.
+int split_geometry(int N, int n_splits, int* keys_per_split) {
+  if (N < 1 || n_splits < 1 || n_splits > FA_MAX_SPLITS) return 0;
+  const int per = (N + n_splits - 1) / n_splits;
+  const int keys = (per + kSplitBR - 1) / kSplitBR * kSplitBR;
+  if (keys_per_split) *keys_per_split = keys;
+  return (N + keys - 1) / keys;
+}
+
+size_t splitkv_bytes(int B, int H, int N, int d, int n_splits) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const int ns = split_geometry(N, n_splits, nullptr);
+  if (ns == 0) return 0;
+  const uint64_t rows = static_cast<uint64_t>(B) * H * N;
+  if (rows > (uint64_t(1) << 40)) return 0;
+  return align_up(static_cast<size_t>(ns) * rows * d * 4) + align_up(static_cast<size_t>(ns) * rows * 4);
+}
+
+size_t fa1_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+  const uint64_t rows = static_cast<uint64_t>(B) * H * N;
+  if (rows > (uint64_t(1) << 40)) return 0;
+  return align_up(rows * d * 4) + 2 * align_up(rows * 4);
+}
+
+// Checks shared by the workspace passes, after validate(): d in {64, 128}, a nonzero
+// scale, a workspace that is large enough, 256-byte aligned and disjoint from the
+// tensors.
+int validate_ws(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* ws, size_t ws_bytes, size_t need, int B, int H, int N, int d,
+                float scale) {
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (scale == 0.f) return FA_ERR_SHAPE;
+  if (!ws) return FA_ERR_NULL;
+  if (need == 0 || ws_bytes < need) return FA_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(ws) & (kWsAlign - 1)) != 0) return FA_ERR_ALIGN;
+  const uint64_t rows = static_cast<uint64_t>(B) * H * N;
+  const uint64_t tb = rows * d * 2, lb = rows * 4;
+  if (ranges_overlap(ws, need, q, tb) || ranges_overlap(ws, need, k, tb) ||
+      ranges_overlap(ws, need, v, tb) || ranges_overlap(ws, need, o, tb) ||
+      ranges_overlap(ws, need, lse, lb))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_splitkv(fa::Params p, int n_eff, hipStream_t stream) {
+  constexpr int WPE = D == 128 ? FA_WPE_D128 : FA_WPE_D64;
+  constexpr int BC = D == 128 ? FA_BC_D128 : FA_BC_D64;
+  p.n_qt = (p.N + kSplitBR - 1) / kSplitBR;
+  const int grid = p.n_qt * p.BH * n_eff;
+  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, BC, WPE, true>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = static_cast<long long>(p.BH) * p.N;
+  const long long blocks = (rows + 15) / 16;
+  hipLaunchKernelGGL((fa::fa_split_merge_kernel<BF16, D>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(256), 0, stream, p.o_part, p.l_part, p.o, p.lse, rows, n_eff);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+int fa_splitkv_impl(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                    size_t ws_bytes, int B, int H, int N, int d, float scale, int causal,
+                    int n_splits, void* stream) {
+  int st = validate(q, k, v, o, lse, B, H, N, d, scale, 0.f);
+  if (st != FA_OK) return st;
+  int keys = 0;
+  const int n_eff = split_geometry(N, n_splits, &keys);
+  if (n_eff == 0) return FA_ERR_SHAPE;
+  const size_t need = splitkv_bytes(B, H, N, d, n_splits);
+  st = validate_ws(q, k, v, o, lse, ws, ws_bytes, need, B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  const int64_t grid = static_cast<int64_t>((N + kSplitBR - 1) / kSplitBR) * B * H * n_eff;
+  if (grid >= (int64_t(1) << 31) / 64) return FA_ERR_SHAPE;
+  fa::Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.N = N;
+  p.d = d;
+  p.BH = B * H;
+  p.c = std::fabs(scale) * 1.4426950408889634f;
+  p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
+  p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
+  p.tau = FA_DEFAULT_RESCALE_LOG2;
+  p.next_stride = 0;
+  p.split_keys = keys;
+  const uint64_t rows = static_cast<uint64_t>(p.BH) * N;
+  p.o_part = static_cast<float*>(ws);
+  p.l_part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                      align_up(static_cast<size_t>(n_eff) * rows * d * 4));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  hipError_t e;
+  if (d == 128) e = cz ? launch_splitkv<BF16, 128, true>(p, n_eff, s) : launch_splitkv<BF16, 128, false>(p, n_eff, s);
+  else e = cz ? launch_splitkv<BF16, 64, true>(p, n_eff, s) : launch_splitkv<BF16, 64, false>(p, n_eff, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <bool BF16>
+int fa_fa1_impl(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
+                size_t ws_bytes, int B, int H, int N, int d, float scale, int causal, void* stream) {
+  int st = validate(q, k, v, o, lse, B, H, N, d, scale, 0.f);
+  if (st != FA_OK) return st;
+  const size_t need = fa1_bytes(B, H, N, d);
+  st = validate_ws(q, k, v, o, lse, ws, ws_bytes, need, B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  fa::Fa1Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  const uint64_t rows = static_cast<uint64_t>(B) * H * N;
+  char* w = static_cast<char*>(ws);
+  p.o_ws = reinterpret_cast<float*>(w);
+  p.m_ws = reinterpret_cast<float*>(w + align_up(rows * d * 4));
+  p.l_ws = reinterpret_cast<float*>(w + align_up(rows * d * 4) + align_up(rows * 4));
+  p.N = N;
+  p.c = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  const dim3 grid(static_cast<unsigned>(B * H)), block(256);
+  if (d == 128) {
+    if (cz) hipLaunchKernelGGL((fa::fa_fwd_fa1_kernel<BF16, 128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa::fa_fwd_fa1_kernel<BF16, 128, false>), grid, block, 0, s, p);
+  } else {
+    if (cz) hipLaunchKernelGGL((fa::fa_fwd_fa1_kernel<BF16, 64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa::fa_fwd_fa1_kernel<BF16, 64, false>), grid, block, 0, s, p);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits) {
+  return splitkv_bytes(B, H, N, d, n_splits);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, int n_splits, int dtype, void* stream) {
+  if (dtype == FA_DTYPE_BF16)
+    return fa_splitkv_impl<true>(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                                 causal, n_splits, stream);
+  if (dtype == FA_DTYPE_FP16)
+    return fa_splitkv_impl<false>(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                                  causal, n_splits, stream);
+  return FA_ERR_UNSUPPORTED;
+}
+
+size_t fa_fwd_fa1_workspace_size(int B, int H, int N, int d) { return fa1_bytes(B, H, N, d); }
+
+int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+               size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+               int dtype, void* stream) {
+  if (dtype == FA_DTYPE_BF16)
+    return fa_fa1_impl<true>(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                             causal, stream);
+  if (dtype == FA_DTYPE_FP16)
+    return fa_fa1_impl<false>(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale,
+                              causal, stream);
+  return FA_ERR_UNSUPPORTED;
+}
+
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int causal, void* stream) {

@@ -87,7 +87,7 @@ struct FastGeom {
   static_assert(2 * PER_WAVE <= NQK, "copies fit in the S^T pipeline steps");
 };
 
-template <bool BF16, int D, bool CAUSAL, int NW, int BC, int WPE>
+template <bool BF16, int D, bool CAUSAL, int NW, int BC, int WPE, bool SPLIT = false>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fa_fwd_fast_kernel(const Params p) {
   using G = FastGeom<D, NW, BC>;
@@ -108,20 +108,47 @@ fa_fwd_fast_kernel(const Params p) {
   const int hh = lane >> 5;
   const int N = p.N;
 
-  int bh, qt;
-  decode_tile<CAUSAL>(p, blockIdx.x, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (SPLIT) {
+    // split-major grid: every split sees the same (head, tile) decode
+    const int per = p.n_qt * p.BH;
+    split = blockIdx.x / per;
+    decode_tile<CAUSAL>(p, blockIdx.x % per, bh, qt);
+  } else {
+    decode_tile<CAUSAL>(p, blockIdx.x, bh, qt);
+  }
+  // keys [kofs, kofs + Nk) of the head; key indices below are relative to kofs (the
+  // whole head unless this is a split-KV partial pass)
+  const int kofs = SPLIT ? split * p.split_keys : 0;
+  const int Nk = SPLIT ? min(N - kofs, p.split_keys) : N;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ qg = p.q + head;
-  const uint16_t* __restrict__ kg = p.k + head;
-  const uint16_t* __restrict__ vg = p.v + head;
+  const uint16_t* __restrict__ kg = p.k + head + (size_t)kofs * D;
+  const uint16_t* __restrict__ vg = p.v + head + (size_t)kofs * D;
 
   const int q0 = qt * G::BR;
   const int wq0 = q0 + wid * 32;
   const int q_end = min(q0 + G::BR, N);
-  const int n_kt = CAUSAL ? (q_end + BC - 1) / BC : (N + BC - 1) / BC;
+  const int n_kt = CAUSAL ? (min(q_end - kofs, Nk) + BC - 1) / BC : (Nk + BC - 1) / BC;
   const bool wave_live = wq0 < N;
   const int w_last_q = min(wq0 + 32, N) - 1;
-  const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
+  const int w_kt = CAUSAL ? min(n_kt, (w_last_q - kofs) / BC + 1) : n_kt;
+  if constexpr (SPLIT) {
+    // Splits start at multiples of the query tile, so under the causal mask a split
+    // either starts at or before q0 (every query of the tile sees its first key) or
+    // after the tile's last query (empty: partial L = -inf, partial O = 0).
+    if (n_kt <= 0) {
+      const int qi = q0 + tid;
+      if (tid < G::BR && qi < N) {
+        const size_t row = ((size_t)split * p.BH + bh) * N + qi;
+        p.l_part[row] = -__builtin_inff();
+        float* orow = p.o_part + row * D;
+        for (int c4 = 0; c4 < D; c4 += 4)
+          *reinterpret_cast<float4*>(orow + c4) = float4{0.f, 0.f, 0.f, 0.f};
+      }
+      return;
+    }
+  }
 
   // ---- HBM -> LDS copies ---------------------------------------------------------
   // Lane `lane` of copy instruction i writes LDS chunk 64 i + lane = (row, physical
@@ -142,7 +169,7 @@ fa_fwd_fast_kernel(const Params p) {
   // so the LDS operand reads of the pipeline keep partial lgkmcnt waits.
   auto copy = [&](const uint16_t* src, u32x4_t* dst, int off, int ii, int j) {
     const int k0 = min(j, n_kt - 1) * BC;
-    const int bytes = min(N - k0, BC) * D * 2;
+    const int bytes = min(Nk - k0, BC) * D * 2;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(src + (size_t)k0 * D), (short)0, bytes, kBufferWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + (wid + ii * NW) * 64), 16,
@@ -240,15 +267,15 @@ fa_fwd_fast_kernel(const Params p) {
   // tiles that reach past N or cross the diagonal need it
   auto mask = [&](STile& s, int j) {
     const int k0 = j * BC;
-    const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > wq0);
+    const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 - kofs);
     if (!masked) return;
-    const int qi = wq0 + l32;
+    const int qi = wq0 + l32 - kofs;  // the query, in key coordinates
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + key_of_reg(r, hh);
-        if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -__builtin_inff();
+        if (key >= Nk || (CAUSAL && key > qi)) s[kb][r] = -__builtin_inff();
       }
   };
 
@@ -398,6 +425,20 @@ fa_fwd_fast_kernel(const Params p) {
   const int qi = wq0 + l32;
   if (qi >= N) return;
   const float inv = 1.0f / l_tot;
+  if constexpr (SPLIT) {
+    const size_t row = ((size_t)split * p.BH + bh) * N + qi;
+    float* prow = p.o_part + row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16_t& a = oacc[db];
+        *reinterpret_cast<float4*>(prow + db * 32 + g * 8 + hh * 4) =
+            float4{a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+      }
+    if (hh == 0) p.l_part[row] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    return;
+  }
   uint16_t* orow = p.o + head + (size_t)qi * D;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)

@@ -161,6 +161,57 @@ def test_backward_validation_errors(L, no_gpu, fn):
     assert fa.fa_last_hip_error() == 0
 
 
+WSA = 0x7f0000000000 + 9 * 0x100000000  # fake workspace address
+
+
+@pytest.mark.parametrize("which", ["splitkv", "fa1"])
+def test_workspace_pass_validation(L, no_gpu, which):
+    G = dict(GOOD, d=64)
+    if which == "splitkv":
+        size = lambda **kw: fa.fa_fwd_splitkv_workspace_size(  # noqa: E731
+            *(dict(G, **kw)[x] for x in ("B", "H", "N", "d")), kw.get("ns", 4))
+
+        def call(ws=WSA, nbytes=None, ns=4, dtype=fa.FA_DTYPE_BF16, o=OA, lse=LA, **kw):
+            a = dict(G, **kw)
+            nb = size(ns=ns) if nbytes is None else nbytes
+            return fa.fa_fwd_splitkv(QA, KA, VA, o, lse, ws, nb, a["B"], a["H"], a["N"],
+                                     a["d"], a["scale"], a["causal"], ns, dtype, None)
+    else:
+        size = lambda **kw: fa.fa_fwd_fa1_workspace_size(  # noqa: E731
+            *(dict(G, **kw)[x] for x in ("B", "H", "N", "d")))
+
+        def call(ws=WSA, nbytes=None, ns=None, dtype=fa.FA_DTYPE_BF16, o=OA, lse=LA, **kw):
+            a = dict(G, **kw)
+            nb = size() if nbytes is None else nbytes
+            return fa.fa_fwd_fa1(QA, KA, VA, o, lse, ws, nb, a["B"], a["H"], a["N"], a["d"],
+                                 a["scale"], a["causal"], dtype, None)
+    rows = G["B"] * G["H"] * G["N"]
+    assert size() >= rows * G["d"] * 4
+    assert size() % 256 == 0
+    assert call(ws=0) == fa.FA_ERR_NULL
+    assert call(nbytes=size() - 1) == fa.FA_ERR_SHAPE
+    assert call(ws=WSA + 16) == fa.FA_ERR_ALIGN
+    assert call(ws=QA) == fa.FA_ERR_ALIAS
+    assert call(ws=LA - 256) == fa.FA_ERR_ALIAS
+    assert call(scale=0.0) == fa.FA_ERR_SHAPE
+    assert call(d=96, nbytes=1 << 30) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=32, nbytes=1 << 30) == fa.FA_ERR_UNSUPPORTED
+    assert call(dtype=2) == fa.FA_ERR_UNSUPPORTED
+    assert call(o=0) == fa.FA_ERR_NULL
+    assert call(o=QA) == fa.FA_ERR_ALIAS
+    assert call(N=0, nbytes=1 << 30) == fa.FA_ERR_SHAPE
+    if which == "splitkv":
+        assert fa.fa_fwd_splitkv_workspace_size(1, 1, 100, 64, 0) == 0
+        assert fa.fa_fwd_splitkv_workspace_size(1, 1, 100, 64, fa.FA_MAX_SPLITS + 1) == 0
+        assert call(ns=0, nbytes=1 << 30) == fa.FA_ERR_SHAPE
+        assert call(ns=fa.FA_MAX_SPLITS + 1, nbytes=1 << 30) == fa.FA_ERR_SHAPE
+        # keys per split are a multiple of 256: N = 1000 with 8 requested splits runs 4
+        per_split = 1000 * 64 * 4 + 1000 * 4
+        assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) <= 4 * per_split + 512
+        assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) >= 4 * per_split
+    assert fa.fa_last_hip_error() == 0
+
+
 def test_inputs_may_alias_each_other(L, no_gpu):
     """q, k, v are read-only and may share memory; that is not an alias error.
     Checked through validation only: with o aliasing q the call must still
