@@ -65,6 +65,18 @@ def _launcher(w, leg="fwd"):
     args = (q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream)
     if leg == "fwd":
         return fn, args
+    dt = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_FP16
+    if leg == "fa1":
+        nb = fa.fa_fwd_fa1_workspace_size(w.B, w.H, w.N, w.d)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+        return fa.fa_fwd_fa1, (q, k, v, o, lse, ws, nb, w.B, w.H, w.N, w.d, w.scale,
+                               int(w.causal), dt, stream)
+    if leg.startswith("splitkv"):
+        ns = int(leg[len("splitkv"):] or 4)
+        nb = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.N, w.d, ns)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda:0")
+        return fa.fa_fwd_splitkv, (q, k, v, o, lse, ws, nb, w.B, w.H, w.N, w.d, w.scale,
+                                   int(w.causal), ns, dt, stream)
     st = fn(*args)
     if st != fa.FA_OK:
         raise fa.FAError(st)
@@ -185,7 +197,32 @@ def _counter_means(directory, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands):
+def io_model(w, path):
+    """Device-memory traffic of one launch by the HBM column of the FA1/FA2 comparison
+    table (currybab.bearblog.dev, "정리": per head FA1 moves 2Nd + T_c Nd + 2 T_c Nd
+    elements, FA2 Nd + 2 T_r Nd + Nd; N-sized statistics omitted), for this kernel's
+    tile sizes and element sizes (16-bit tensors; the FA1 kernel keeps O_i, m_i, l_i in
+    float32 and skips the read before the first key block)."""
+    heads = w.B * w.H
+    nd = w.N * w.d
+    if path == "fa1":
+        t_c = -(-w.N // 64)
+        fetch = 2 * 2 * nd + 2 * t_c * nd + 4 * (t_c - 1) * nd + 8 * (t_c - 1) * w.N
+        write = 4 * (t_c - 1) * nd + 2 * nd + 8 * (t_c - 1) * w.N + 4 * w.N
+        elems = 2 * nd + 3 * t_c * nd
+        blocks = {"T_c": t_c}
+    else:
+        t_r = -(-w.N // 256)
+        fetch = 2 * nd + 2 * 2 * t_r * nd
+        write = 2 * nd + 4 * w.N
+        elems = 2 * nd + 2 * t_r * nd
+        blocks = {"T_r": t_r}
+    return {"table_elements_per_launch": heads * elems, **blocks,
+            "model_fetch_bytes": heads * fetch, "model_write_bytes": heads * write,
+            "note": "non-causal; the table assumes every re-read reaches device memory"}
+
+
+def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands, path="fwd"):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
     HBM bytes per launch of the attention kernel, each counter scaled by what it reads
     for the plain copy of copy_mib MiB in the same run."""
@@ -194,7 +231,8 @@ def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands):
     w = workloads.get(workload)
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
-    fa_name = next(k for k in fetch if "fa_fwd" in k)
+    key = "fa_fwd_fa1" if path == "fa1" else "fa_fwd_wide"
+    fa_name = next(k for k in fetch if key in k)
     copy_name = next(k for k in fetch if "MulFunctor" in k)
     copy_kib = copy_mib * 1024.0
     f_scale = copy_kib / fetch[copy_name]
@@ -210,6 +248,9 @@ def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands):
         "hbm_bytes_per_launch": fa_bytes,
         "algorithmic_bytes_per_launch": w.min_bytes(),
         "traffic_over_algorithmic": fa_bytes / w.min_bytes(),
+        "fetch_bytes_per_launch": fetch[fa_name] * f_scale * 1024.0,
+        "write_bytes_per_launch": write[fa_name] * w_scale * 1024.0,
+        "io_model": io_model(w, path),
         "commands": commands,
     }
     with open(out_path, "w") as f:
@@ -258,6 +299,9 @@ def main(argv=None):
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--also", default="causal8k,long32k,stress4000",
                     help="extra workloads timed for the 'workloads' field ('' for none)")
+    ap.add_argument("--path", default="fwd",
+                    help="with --summarize-hbm or for profiling runs: fwd (the FA2-order "
+                         "forward, the default and the headline), bwd, fa1, splitkvS")
     ap.add_argument("--backward", default="ai2048,causal8k,long32k,stress4000",
                     help="workloads whose backward pass is also timed (comma list; empty: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -267,9 +311,10 @@ def main(argv=None):
     ap.add_argument("--commands", default="", help="commands recorded in the summary")
     a = ap.parse_args(argv)
     if a.summarize_hbm:
-        out = os.path.join(ROOT, "profiles", f"fa_fwd_{a.workload}_hbm_counters.json")
+        stem = "fa_fwd" if a.path == "fwd" else f"fa_{a.path}"
+        out = os.path.join(ROOT, "profiles", f"{stem}_{a.workload}_hbm_counters.json")
         rec = summarize_hbm(a.workload, a.summarize_hbm[0], a.summarize_hbm[1],
-                            a.calibrate_copy_mib, out, a.commands)
+                            a.calibrate_copy_mib, out, a.commands, a.path)
         print(json.dumps(rec))
         return 0
     if a.gpus != 1:
@@ -287,6 +332,14 @@ def main(argv=None):
     if a.calibrate_copy_mib:
         calibrate_copy(a.calibrate_copy_mib)
     w = workloads.get(a.workload)
+    if a.path != "fwd":
+        # one pass other than the headline forward, for profiling runs
+        msx, wallx, ranx = time_gpu(w, a.steps, a.warmup, leg=a.path)
+        work = 2.5 * w.flops() if a.path == "bwd" else w.flops()
+        print(json.dumps({"path": a.path, "workload": w.name, "ms": round(msx, 5),
+                          "tflops": round(work / (msx * 1e-3) / 1e12, 2),
+                          "steps": a.steps, "warmup_steps_run": ranx}), flush=True)
+        return 0
     ms, wall, warm_ran = time_gpu(w, a.steps, a.warmup)
     tflops = w.flops() / (ms * 1e-3) / 1e12
     traffic = measured_traffic(w.name)
