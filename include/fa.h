@@ -135,6 +135,31 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
               float rescale_log2, void* stream);
 
 /*
+ * fa_fwd_fp8 — the operation of fa_fwd on 8-bit inputs: q, k, v hold OCP FP8 E4M3
+ * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F/0xFF NaN, no
+ * infinity) with one float scale per tensor, so Q = q_scale * decode(q), and likewise for
+ * K and V. Computes O = softmax(scale * Q K^T [+ causal mask]) V and L exactly as fa_fwd
+ * defines them, on the decoded tensors, with 8-bit matrix products: the FP8 path of [P2]
+ * "v2와 v3" (FP8 doubling the matrix throughput of 16-bit inputs).
+ *
+ * Numerics: Q K^T accumulates the 8-bit products in float32; the online softmax runs
+ * in float32; the unnormalised probabilities are rounded to E4M3 (round to nearest
+ * even, 3 mantissa bits) for the P V product, which makes O differ from the exact
+ * result by up to a few 2^-4 relative errors of each probability (L does not see that
+ * rounding). O is written as bfloat16 (RNE), L as float32.
+ *
+ * Arguments: q, k, v device pointers to contiguous row-major [B, H, N, d] byte tensors,
+ * 16-byte aligned; o a bfloat16 [B, H, N, d] output, 16-byte aligned; lse float32
+ * [B, H, N]. d must be 64 or 128 (FA_ERR_UNSUPPORTED). scale and the three tensor scales
+ * must be finite and scale * q_scale * k_scale nonzero (FA_ERR_SHAPE). Ownership,
+ * aliasing (o, lse may not overlap the inputs or each other), errors and asynchrony as
+ * fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+               float v_scale, void* o, float* lse, int B, int H, int N, int d, float scale,
+               int causal, void* stream);
+
+/*
  * fa_fwd_splitkv — the operation of fa_fwd_ex (same outputs, up to rounding), with the
  * keys of every head split into ranges that separate workgroups process, for shapes
  * whose B * H * ceil(N / 256) query tiles are too few to fill the GPU (few heads,

@@ -23,6 +23,7 @@ __all__ = [
     "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
     "fa_bwd", "fa_bwd_fp16", "backward", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
     "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "forward_splitkv", "forward_fa1", "FA_MAX_SPLITS",
+    "fa_fwd_fp8", "forward_fp8",
     "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
 ]
@@ -37,7 +38,7 @@ FA_ERR_HIP = -6
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
-EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
            "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
            "fa_strerror", "fa_last_hip_error", "fa_version")
 FA_MAX_SPLITS = 64
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, f, vp]
     L.fa_fwd_ex.restype = i
     sz = ctypes.c_size_t
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, f, i, vp]
+    L.fa_fwd_fp8.restype = i
     L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, i, vp]
     L.fa_fwd_splitkv.restype = i
     L.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
@@ -136,6 +139,14 @@ def fa_fwd_ex(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, rescale_log2,
     return lib().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                            float(scale), int(causal), int(dtype), float(rescale_log2),
                            _stream(stream))
+
+
+def fa_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale, causal,
+               stream=None) -> int:
+    """C ``fa_fwd_fp8``: E4M3 codes with per-tensor scales in, bfloat16 O out."""
+    return lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), float(q_scale), float(k_scale),
+                            float(v_scale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                            int(causal), _stream(stream))
 
 
 def fa_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scale, causal,
@@ -326,3 +337,33 @@ def forward_fa1(q, k, v, causal: bool = False, scale: float | None = None, strea
     """O, L in the FA1 loop order (``fa_fwd_fa1``, an ablation); d = 64 or 128."""
     return _workspace_call("fa_fwd_fa1", fa_fwd_fa1_workspace_size, fa_fwd_fa1,
                            q, k, v, causal, scale, stream, (), workspace)
+
+
+def forward_fp8(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float,
+                causal: bool = False, scale: float | None = None, stream=None):
+    """O (bfloat16), L for contiguous [B, H, N, d] uint8 (or float8_e4m3fn) CUDA tensors of
+    E4M3 codes with per-tensor scales (``fa_fwd_fp8``); d = 64 or 128."""
+    import torch
+
+    ts = (q8, k8, v8)
+    if any(t.element_size() != 1 for t in ts):
+        raise ValueError("q8, k8, v8 must be 1-byte tensors of E4M3 codes")
+    if q8.dim() != 4 or any(t.shape != q8.shape for t in ts):
+        raise ValueError("q8, k8, v8 must have the same [B, H, N, d] shape")
+    if not q8.is_cuda or any(t.device != q8.device for t in ts):
+        raise ValueError("q8, k8, v8 must be on the same GPU")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("q8, k8, v8 must be contiguous")
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device)
+    with torch.cuda.device(q8.device):
+        st = fa_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, out, lse, B, H, N, d, scale,
+                        causal, stream)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
+    return out, lse

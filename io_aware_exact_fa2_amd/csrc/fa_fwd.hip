@@ -3,6 +3,7 @@
 #include "fa.h"
 #include "fa_fwd_fa1.hpp"
 #include "fa_fwd_fast.hpp"
+#include "fa_fwd_fp8.hpp"
 #include "fa_fwd_split.hpp"
 #include "fa_fwd_generic.hpp"
 #include "fa_fwd_wide.hpp"
@@ -322,9 +323,80 @@ int fa_fa1_impl(const void* q, const void* k, const void* v, void* o, float* lse
   return FA_OK;
 }
 
+// ---- 8-bit (e4m3) forward --------------------------------------------------------
+constexpr float kFp8Tau = 0.0f;  // literal per-block max update: probabilities <= 1
+
+template <int D, bool CAUSAL>
+hipError_t launch_fp8(fa::Fp8Params p, hipStream_t stream) {
+  p.n_qt = (p.N + 255) / 256;
+  const int grid = p.n_qt * p.BH;
+  hipLaunchKernelGGL((fa::fa_fwd_fp8_kernel<D, CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
+int fa_fp8_impl(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                float v_scale, void* o, float* lse, int B, int H, int N, int d, float scale,
+                int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_SHAPE;
+  if (!std::isfinite(scale) || !std::isfinite(q_scale) || !std::isfinite(k_scale) ||
+      !std::isfinite(v_scale))
+    return FA_ERR_SHAPE;
+  const double cs = static_cast<double>(scale) * q_scale * k_scale;
+  if (cs == 0.0 || !std::isfinite(cs) || std::fabs(cs) * 1.4426950408889634 > 3.0e38)
+    return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(N) * d >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  const int64_t bh = static_cast<int64_t>(B) * H;
+  if (bh >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+  const int64_t rows = bh * N;
+  if (rows > (int64_t(1) << 54)) return FA_ERR_SHAPE;
+  if (((N + 255) / 256) * bh >= (int64_t(1) << 31) / 64) return FA_ERR_SHAPE;
+  const uintptr_t a16 = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o);
+  if ((a16 & 15u) != 0 || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_ALIGN;
+  const uint64_t ib = static_cast<uint64_t>(rows) * d, ob = ib * 2, lb = rows * 4;
+  if (ranges_overlap(o, ob, q, ib) || ranges_overlap(o, ob, k, ib) || ranges_overlap(o, ob, v, ib) ||
+      ranges_overlap(lse, lb, q, ib) || ranges_overlap(lse, lb, k, ib) ||
+      ranges_overlap(lse, lb, v, ib) || ranges_overlap(lse, lb, o, ob))
+    return FA_ERR_ALIAS;
+  fa::Fp8Params p;
+  p.q = static_cast<const uint8_t*>(q);
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.N = N;
+  p.BH = static_cast<int>(bh);
+  p.n_qt = 0;
+  p.c = static_cast<float>(std::fabs(cs) * 1.4426950408889634);
+  p.qsign = cs < 0.0 ? 0x80808080u : 0u;
+  p.vs = v_scale;
+  p.tau = kFp8Tau;
+  p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool cz = causal != 0;
+  hipError_t e;
+  if (d == 128) e = cz ? launch_fp8<128, true>(p, s) : launch_fp8<128, false>(p, s);
+  else e = cz ? launch_fp8<64, true>(p, s) : launch_fp8<64, false>(p, s);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+               float v_scale, void* o, float* lse, int B, int H, int N, int d, float scale,
+               int causal, void* stream) {
+  return fa_fp8_impl(q, k, v, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale, causal,
+                     stream);
+}
+
 
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits) {
   return splitkv_bytes(B, H, N, d, n_splits);

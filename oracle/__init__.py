@@ -27,6 +27,8 @@ Modules:
   merge, FA2 and FA1 loop orders) in float64, used to pin the pages' claims.
 * ``backward``   — the gradients of the same definition (dQ, dK, dV) in float64,
   the reference for the backward pass that recomputes P from L.
+* ``fp8``        — the OCP E4M3 decoder and attention on decoded 8-bit inputs with
+  per-tensor scales, the reference for the 8-bit forward.
 
 Every function here is pinned by ``tests/test_oracle_pins.py``; none is
 "parity unpinned".
@@ -34,7 +36,8 @@ Every function here is pinned by ``tests/test_oracle_pins.py``; none is
 from .attention import attention, attention_rows
 from .bruteforce import attention_bruteforce
 from .backward import attention_backward
+from .fp8 import attention_fp8, attention_fp8_rows, decode_e4m3
 from . import online
 
 __all__ = ["attention", "attention_rows", "attention_bruteforce", "attention_backward",
-           "online"]
+           "attention_fp8", "attention_fp8_rows", "decode_e4m3", "online"]

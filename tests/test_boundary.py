@@ -212,6 +212,30 @@ def test_workspace_pass_validation(L, no_gpu, which):
     assert fa.fa_last_hip_error() == 0
 
 
+def test_fp8_validation(L, no_gpu):
+    def call(q=QA, k=KA, v=VA, o=OA, lse=LA, qs=0.01, ks=0.01, vs=0.01, **kw):
+        a = dict(GOOD, **kw)
+        return fa.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, a["B"], a["H"], a["N"], a["d"],
+                             a["scale"], a["causal"], None)
+    for name in ("q", "k", "v", "o", "lse"):
+        assert call(**{name: 0}) == fa.FA_ERR_NULL, name
+    for bad in (dict(B=0), dict(N=0), dict(H=-1)):
+        assert call(**bad) == fa.FA_ERR_SHAPE, bad
+    for kw in (dict(scale=0.0), dict(qs=0.0), dict(ks=float("nan")), dict(vs=float("inf")),
+               dict(scale=float("inf"))):
+        assert call(**kw) == fa.FA_ERR_SHAPE, kw
+    for d in (1, 32, 96, 127, 129):
+        assert call(d=d) == fa.FA_ERR_UNSUPPORTED, d
+    assert call(q=QA + 8) == fa.FA_ERR_ALIGN
+    assert call(lse=LA + 1) == fa.FA_ERR_ALIGN
+    # o holds 2-byte elements over 1-byte inputs: its second half overlapping v is caught
+    ib = GOOD["B"] * GOOD["H"] * GOOD["N"] * GOOD["d"]
+    assert call(o=VA - ib) == fa.FA_ERR_ALIAS
+    assert call(lse=OA + 2 * ib - 16) == fa.FA_ERR_ALIAS
+    assert call(o=QA) == fa.FA_ERR_ALIAS
+    assert fa.fa_last_hip_error() == 0
+
+
 def test_inputs_may_alias_each_other(L, no_gpu):
     """q, k, v are read-only and may share memory; that is not an alias error.
     Checked through validation only: with o aliasing q the call must still

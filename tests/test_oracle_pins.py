@@ -503,3 +503,63 @@ def test_backward_linear_in_do():
     c = oracle.attention_backward(q, k, v, 2.0 * do - 3.0 * do2, 0.6, False)
     for x, y, z in zip(a, b, c):
         np.testing.assert_allclose(z, 2.0 * x - 3.0 * y, atol=1e-12)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 decoding
+def test_e4m3_decoder_named_values():
+    """Values the OCP E4M3 definition fixes: 1.0, the largest finite (448), the
+    smallest normal (2^-6) and subnormal (2^-9), signed zero, NaN at 0x7F / 0xFF."""
+    d = oracle.decode_e4m3
+    assert d(0x38) == 1.0 and d(0xB8) == -1.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0
+    assert d(0x08) == 2.0 ** -6 and d(0x07) == 7 * 2.0 ** -9 and d(0x01) == 2.0 ** -9
+    assert d(0x00) == 0.0 and np.signbit(d(0x80))
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    assert d(0x30) == 0.5 and d(0x40) == 2.0 and d(0x2A) == 0.3125
+
+
+def test_e4m3_decoder_matches_torch_for_every_code():
+    """All 256 codes against torch's float8_e4m3fn conversion (an independent decoder)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    # monotone over the positive finite codes, and the round trip of the generator
+    pos = got[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_attention_fp8_is_attention_of_the_decoded_inputs():
+    """Codes whose decoded values are small dyadic numbers: the 8-bit oracle equals the
+    brute force on the decoded tensors, and the per-tensor scales act as Q·qs etc."""
+    rng = np.random.default_rng(99)
+    shape = (1, 2, 6, 4)
+    # exponent fields 6..8 -> |value| in [0.5, 4): exact in float64
+    codes = [((rng.integers(0, 2, shape) << 7) | (rng.integers(6, 9, shape) << 3)
+              | rng.integers(0, 8, shape)).astype(np.uint8) for _ in range(3)]
+    qs, ks, vs, scale = 0.25, 2.0, 0.5, 0.7
+    for causal in (False, True):
+        O, L = oracle.attention_fp8(*codes, qs, ks, vs, scale, causal)
+        q, k, v = (oracle.decode_e4m3(c) for c in codes)
+        Ob, Lb = oracle.attention_bruteforce(q * qs, k * ks, v * vs, scale, causal)
+        np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, Lb, rtol=0, atol=1e-12)
+        # scales fold into the scores and the output
+        O2, L2 = oracle.attention(q, k, v, scale * qs * ks, causal)
+        np.testing.assert_allclose(O, O2 * vs, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L, L2, rtol=0, atol=1e-12)
+
+
+def test_fp8_generator_codes_round_trip():
+    """The input generator's codes decode to within one E4M3 rounding of the draws and
+    use the full range (the largest magnitude maps to 448)."""
+    w = workloads.Workload("f8", 1, 2, 64, 64, "bf16", False, seed=5)
+    q8, k8, v8, qs, ks, vs = workloads.make_fp8_inputs(w)
+    for c, s in ((q8, qs), (k8, ks), (v8, vs)):
+        x = oracle.decode_e4m3(c.numpy())
+        assert np.isfinite(x).all()
+        assert np.abs(x).max() == 448.0
+        assert s > 0

@@ -38,7 +38,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_grad", "to_f64", "scaled"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_grad", "make_fp8_inputs",
+           "to_f64", "scaled"]
 
 
 @dataclass(frozen=True)
@@ -128,6 +129,30 @@ def make_grad(w: Workload, seed: int | None = None) -> torch.Tensor:
     rng = np.random.Generator(np.random.PCG64(w.seed + 10007 if seed is None else seed))
     g = rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32)
     return _round(g, w.torch_dtype)
+
+
+def make_fp8_inputs(w: Workload, seed: int | None = None):
+    """The workload's Q, K, V (drawn as by ``make_inputs``, before the 16-bit rounding)
+    encoded as FP8 E4M3 codes with one scale per tensor: scale = max|x| / 448 (the
+    largest E4M3 value), code = E4M3(x / scale) by torch's float8_e4m3fn conversion
+    (round to nearest even). Returns (q8, k8, v8) as uint8 CPU tensors and the three
+    scales as Python floats."""
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    shape = (w.B, w.H, w.N, w.d)
+    if w.dist == "normal":
+        xs = [rng.standard_normal(shape, dtype=np.float32) for _ in range(3)]
+    elif w.dist == "stress":
+        q, k, v = make_inputs(replace(w, dtype="bf16"), seed)  # same draws, incl. spikes
+        xs = [t.float().numpy() for t in (q, k, v)]
+    else:
+        raise ValueError(f"unknown distribution {w.dist!r}")
+    out, scales = [], []
+    for x in xs:
+        s = float(np.abs(x).max()) / 448.0
+        t = torch.from_numpy(np.ascontiguousarray(x / np.float32(s), dtype=np.float32))
+        out.append(t.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+        scales.append(s)
+    return out[0], out[1], out[2], scales[0], scales[1], scales[2]
 
 
 def spike_rows(w: Workload, seed: int | None = None):
