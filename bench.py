@@ -24,6 +24,7 @@ METRIC = "FA fwd TFLOPS (4·B·H·N²·d, causal halved) and % of bf16 MFMA peak
 PEAK_TFLOPS = 2500.0        # MI355X dense bf16/fp16 MFMA, published
 WARMUP_MIN_S = 0.3          # least back-to-back warmup before the timed steps (clock ramp)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak, published
 CSRC = os.path.join(ROOT, "io_aware_exact_fa2_amd", "csrc")
 
 
@@ -57,10 +58,16 @@ def _launcher(w, leg="fwd"):
     import io_aware_exact_fa2_amd as fa
     import workloads
 
+    stream = torch.cuda.current_stream()
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    if leg == "fp8":
+        q8, k8, v8, qs, ks, vs = workloads.make_fp8_inputs(w)
+        q8, k8, v8 = (t.to("cuda:0") for t in (q8, k8, v8))
+        o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda:0")
+        return fa.fa_fwd_fp8, (q8, k8, v8, qs, ks, vs, o, lse, w.B, w.H, w.N, w.d, w.scale,
+                               int(w.causal), stream)
     q, k, v = (t.to("cuda:0") for t in workloads.make_inputs(w))
     o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
-    stream = torch.cuda.current_stream()
     fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_fp16
     args = (q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, int(w.causal), stream)
     if leg == "fwd":
@@ -304,6 +311,8 @@ def main(argv=None):
                          "forward, the default and the headline), bwd, fa1, splitkvS")
     ap.add_argument("--backward", default="ai2048,causal8k,long32k,stress4000",
                     help="workloads whose backward pass is also timed (comma list; empty: none)")
+    ap.add_argument("--fp8", default="ai2048,causal8k,long32k",
+                    help="workloads whose 8-bit (E4M3) forward is also timed (empty: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-hbm", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -365,6 +374,16 @@ def main(argv=None):
                      "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1), "dtype": wx.dtype,
                      "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d],
                      "flops": "2.5 x forward: five N x N x d products (dV, dP, dQ, dK, S)"}
+    f8 = {}
+    for name in [s for s in a.fp8.split(",") if s]:
+        wx = workloads.get(name)
+        msx, _, _ = time_gpu(wx, max(5, a.steps // 5), 3, leg="fp8")
+        tx = wx.flops() / (msx * 1e-3) / 1e12
+        f8[name] = {"ms": round(msx, 4), "tflops": round(tx, 1),
+                    "pct_fp8_peak": round(100 * tx / PEAK_FP8_TFLOPS, 1),
+                    "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1),
+                    "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d],
+                    "inputs": "E4M3 codes with per-tensor scales, bf16 O"}
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -391,6 +410,7 @@ def main(argv=None):
         "cold": cold,
         "workloads": extra,
         "backward": bwd,
+        "fp8": f8,
     }
     if a.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)
