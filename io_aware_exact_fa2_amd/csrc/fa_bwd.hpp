@@ -27,6 +27,10 @@
 
 #include "fa_common.hpp"
 
+#ifndef FA_BWD_PIPE
+#define FA_BWD_PIPE 0
+#endif
+
 namespace fa {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -60,8 +64,8 @@ template <int D> __device__ __forceinline__ int swz_b(int row) {
 }
 
 // Rows [r0, r0 + ROWS) of a [N, D] matrix held in registers on their way to LDS: all
-// threads of the workgroup load whole 16-byte chunks (rows at or past N as zeros), so
-// the next tile's loads can be in flight while the current tile is computed.
+// threads of the workgroup load whole 16-byte chunks, so the next tile's loads can be in
+// flight while the current tile is computed.
 template <int D, int ROWS, int NT>
 struct BwdTile {
   static constexpr int CPR = D / 8, PER = ROWS * CPR / NT;
@@ -69,12 +73,14 @@ struct BwdTile {
   u32x4_t x[PER];
   // chunk t of this thread: row tid / CPR + t * NT / CPR, chunk tid % CPR
   static __device__ __forceinline__ int row_of(int tid, int t) { return (tid + NT * t) / CPR; }
+  // Rows past N repeat row N - 1: finite data whose probabilities the kernels' masks set
+  // to zero, so every score, P and dS of such a row is 0 or masked. No select or branch
+  // touches the loaded value, so its wait stays at the store, after the current tile.
   __device__ __forceinline__ void load(const uint16_t* src, int r0, int N, int tid) {
 #pragma unroll
     for (int t = 0; t < PER; ++t) {
       const int row = row_of(tid, t), ch = tid % CPR;
-      x[t] = u32x4_t{0u, 0u, 0u, 0u};
-      if (r0 + row < N) x[t] = ld16(src + (size_t)(r0 + row) * D + ch * 8);
+      x[t] = ld16(src + (size_t)min(r0 + row, N - 1) * D + ch * 8);
     }
   }
   __device__ __forceinline__ void store(u32x4_t* lds, int tid) const {
@@ -129,9 +135,9 @@ template <int D>
 __device__ __forceinline__ u32x4_t bwd_tr_frag(const u32x4_t* tile, const uint32_t (&off)[D / 32][2],
                                                int db, int st) {
   constexpr int CPR = D / 8;
-  const uint32_t b = (uint32_t)(uintptr_t)tile + 16 * st * CPR * 16;
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(b + off[db][0]));
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(b + off[db][1]));
+  const unsigned char* b = reinterpret_cast<const unsigned char*>(tile) + 16 * st * CPR * 16;
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b + off[db][0]));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b + off[db][1]));
   const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
   return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
 }
@@ -319,7 +325,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int t = 0; t < Tile::PER; ++t) {
       const int q = qb0 + Tile::row_of(tid, t);
-      ln[t] = q < N ? p.lse[(size_t)bh * N + q] : 0.f;
+      ln[t] = p.lse[(size_t)bh * N + min(q, N - 1)];  // rows past N: masked
     }
   };
   fetch(i0 * BQ);
@@ -346,17 +352,27 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
     __syncthreads();
     if (i + 1 < n_qt) fetch(qb0 + BQ);
     if (!wave_live) continue;
+    // Per 32-query block: S and dP (MFMA), the softmax terms (VALU), dV and dK (MFMA).
+    // At d = 128 both blocks' S and dP are issued first, so block 1's products run while
+    // block 0's softmax terms are computed, and block 1's softmax while block 0's dV, dK
+    // run.
+    auto sdp = [&](int qb, f32x16_t& s, f32x16_t& dp) {
 #pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      // S and dP of these 32 queries x this wave's 32 keys (row = query, lane = key)
-      f32x16_t s = {}, dp = {};
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         s = E::mfma(bwd_row_frag<D>(qs, 32 * qb, l32, hh, ds), kf[ds], s);
         dp = E::mfma(bwd_row_frag<D>(dos, 32 * qb, l32, hh, ds), vf[ds], dp);
       }
-      // L and D of the rows: register r holds query qb0 + 32 qb + 8 hh + rc(r), with
-      // rc(r) = (r & 7) + 16 (r >> 3); it sees this lane's key when lo <= rc(r) < hi
+    };
+    // P and dS as 16-bit B operands. L and D of the rows: register r holds query
+    // qb0 + 32 qb + 8 hh + rc(r), with rc(r) = (r & 7) + 16 (r >> 3); it sees this
+    // lane's key when lo <= rc(r) < hi
+    auto soft = [&](int qb, const f32x16_t& s, const f32x16_t& dp, u32x4_t (&pop)[2],
+                    u32x4_t (&dsop)[2]) {
       f32x4_t lv[4], dv4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -367,23 +383,28 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
       const int base = qb0 + 32 * qb + 8 * hh;
       const int lo = CAUSAL ? kj - base : -32;
       const int hi = kj < N ? N - base : -32;
-      u32x4_t pop[2], dsop[2];
+      auto body = [&](bool masked) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float pv[2], dv2[2];
+        for (int r = 0; r < 16; r += 2) {
+          float pv[2], dv2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int re = r + e, rc = key_of_reg(re, 0);
-          const float pr = (rc >= lo && rc < hi)
-                               ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[re], p.c, -lv[re / 4][re % 4]))
-                               : 0.f;
-          pv[e] = pr;
-          dv2[e] = pr * (dp[re] - dv4[re / 4][re % 4]);
+          for (int e = 0; e < 2; ++e) {
+            const int re = r + e, rc = key_of_reg(re, 0);
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[re], p.c, -lv[re / 4][re % 4]));
+            if (masked && !(rc >= lo && rc < hi)) pr = 0.f;
+            pv[e] = pr;
+            dv2[e] = pr * (dp[re] - dv4[re / 4][re % 4]);
+          }
+          pop[r / 8][(r % 8) / 2] = E::pack(pv[0], pv[1]);
+          dsop[r / 8][(r % 8) / 2] = E::pack(dv2[0], dv2[1]);
         }
-        pop[r / 8][(r % 8) / 2] = E::pack(pv[0], pv[1]);
-        dsop[r / 8][(r % 8) / 2] = E::pack(dv2[0], dv2[1]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries (two 16-query steps)
+      };
+      // every register r (rc(r) in [0, 32)) allowed in every lane: no per-score mask
+      if (D == 128 && __builtin_amdgcn_ballot_w64(!(lo <= 0 && hi >= 32)) == 0) body(false);
+      else body(true);
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS over 32 queries (two 16-query steps)
+    auto accum = [&](int qb, const u32x4_t (&pop)[2], const u32x4_t (&dsop)[2]) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -391,6 +412,26 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
           dv[db] = E::mfma(bwd_tr_frag<D>(dos, troff, db, 2 * qb + s2), pop[s2], dv[db]);
           dk[db] = E::mfma(bwd_tr_frag<D>(qs, troff, db, 2 * qb + s2), dsop[s2], dk[db]);
         }
+    };
+    static_assert(BQ == 64, "two 32-query blocks per tile");
+    if constexpr (D == 128 && FA_BWD_PIPE) {  // both blocks' S and dP first
+      f32x16_t s0, dp0, s1, dp1;
+      u32x4_t pop0[2], dsop0[2], pop1[2], dsop1[2];
+      sdp(0, s0, dp0);
+      sdp(1, s1, dp1);
+      soft(0, s0, dp0, pop0, dsop0);
+      accum(0, pop0, dsop0);
+      soft(1, s1, dp1, pop1, dsop1);
+      accum(1, pop1, dsop1);
+    } else {  // d = 64 keeps two waves per SIMD with one block at a time
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16_t s, dp;
+        u32x4_t pop[2], dsop[2];
+        sdp(qb, s, dp);
+        soft(qb, s, dp, pop, dsop);
+        accum(qb, pop, dsop);
+      }
     }
   }
   if (wave_live && kj < N) {
