@@ -19,7 +19,8 @@
 // exactly the 32 consecutive keys that lane half h supplies as the B operand of the
 // 64-key P V product. V^T operands are read with ds_read_b64_tr_b8 (each lane of a
 // 16-lane group receives one column of 8 rows). Tiles are staged through registers, the
-// next tile's loads in flight while the current one is computed.
+// next tile's loads in flight while the current one is computed. Workgroups of NW waves
+// of 32 queries each (4 by default: three workgroups share a CU).
 #pragma once
 
 #include "fa_common.hpp"
@@ -58,10 +59,14 @@ template <int D> __device__ __forceinline__ int swz8_v(int row) {
   return D == 128 ? 2 * ((row >> 1) & 3) : 2 * ((row >> 2) & 1);
 }
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+#ifndef FA_FP8_WPE
+#define FA_FP8_WPE 2  // least waves per SIMD the register budget must allow
+#endif
+
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_FP8_WPE)))
 fa_fwd_fp8_kernel(const Fp8Params p) {
-  constexpr int NW = 8, BR = NW * 32, BC = 64, CPR = D / 16;  // 16-byte chunks per row
+  constexpr int BR = NW * 32, BC = 64, CPR = D / 16;  // 16-byte chunks per row
   constexpr int NT = D / 64;                                  // 64-deep MFMA steps over d
   constexpr int TOT = BC * CPR;                               // chunks per tile and tensor
   constexpr int PER = (TOT + NW * 64 - 1) / (NW * 64);        // chunks per thread per tile
@@ -147,7 +152,7 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
     return r;
   };
 
-  // staging: thread chunk t -> row (tid + 512 t) / CPR, chunk tid % CPR (threads past
+  // staging: thread chunk t -> row (tid + 64 NW t) / CPR, chunk tid % CPR (threads past
   // the tile's chunks idle)
   u32x4_t kn[PER], vn[PER];
   auto fetch = [&](int j) {
