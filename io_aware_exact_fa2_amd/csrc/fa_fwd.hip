@@ -324,18 +324,36 @@ int fa_fa1_impl(const void* q, const void* k, const void* v, void* o, float* lse
 }
 
 // ---- 8-bit (e4m3) forward --------------------------------------------------------
-constexpr float kFp8Tau = 0.0f;  // literal per-block max update: probabilities <= 1
+constexpr float kFp8Tau = 2.0f;  // probabilities <= 4 before the 2^6 scale (<= 256 < 448)
 #ifndef FA_FP8_NW
 #define FA_FP8_NW 4  // waves (32 queries each) per workgroup of the 8-bit kernel (8: -8..18%)
 #endif
+
+// Workgroups of equal length (no causal mask) run in rounds: with three resident per CU a
+// grid of W workgroups takes ceil(W / 3C) rounds of three-way shared SIMDs, with two
+// ceil(W / 2C) rounds of two-way shared ones (C = CU count). When the second is shorter
+// (e.g. W = 4C: 2 rounds at two per CU against 1.33, i.e. 2, rounds at three with the
+// last one a third full), unused dynamic LDS caps residency at two workgroups per CU.
+// The 1.15 is the measured throughput gain of the third resident workgroup.
+size_t fp8_lds_cap(int grid, bool causal, size_t static_lds) {
+  const int cus = fa_host::cu_count();
+  if (causal || cus <= 0 || FA_FP8_NW != 4) return 0;
+  const double r3 = std::ceil(grid / (3.0 * cus)) * 3.0 / 1.15;
+  const double r2 = std::ceil(grid / (2.0 * cus)) * 2.0;
+  if (r2 >= r3) return 0;
+  const size_t per_cu = 160 * 1024, want = per_cu / 2 - 1024;  // two fit, three do not
+  return want > static_lds ? want - static_lds : 0;
+}
 
 template <int D, bool CAUSAL>
 hipError_t launch_fp8(fa::Fp8Params p, hipStream_t stream) {
   constexpr int BR = FA_FP8_NW * 32;
   p.n_qt = (p.N + BR - 1) / BR;
   const int grid = p.n_qt * p.BH;
+  const size_t static_lds = 2 * 2 * 64 * D;  // two K and two V tiles of 64 rows
+  const size_t dyn = fp8_lds_cap(grid, CAUSAL, static_lds);
   hipLaunchKernelGGL((fa::fa_fwd_fp8_kernel<D, CAUSAL, FA_FP8_NW>), dim3(grid),
-                     dim3(FA_FP8_NW * 64), 0, stream, p);
+                     dim3(FA_FP8_NW * 64), dyn, stream, p);
   return hipGetLastError();
 }
 

@@ -7,11 +7,12 @@
 //     are S = scale * qs * ks * (Q8 K8^T), accumulated in fp32 by
 //     v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales);
 //   * the online softmax (running max, rescale by alpha, sum l) runs in fp32 as in the
-//     16-bit kernels, with the literal per-block max update, so the unnormalised
-//     probabilities stay at or below 1; they are scaled by 2^8 (folded into the exponent;
-//     the factor cancels between O and l) and rounded to e4m3 for the P V product: at
-//     most 256 < 448, the largest e4m3 value, and normal (3 mantissa bits) down to 2^-14
-//     of the row's max, where the format's subnormal range begins. l sums them unrounded;
+//     16-bit kernels; a row's reference max is raised only when a block's max exceeds it
+//     by more than tau = 2 (log2 units), so the unnormalised probabilities stay at or
+//     below 4; they are scaled by 2^6 (folded into the exponent; the factor cancels
+//     between O and l) and rounded to e4m3 for the P V product: at most 256 < 448, the
+//     largest e4m3 value, and normal (3 mantissa bits) down to 2^-12 of the reference,
+//     where the format's subnormal range begins. l sums them unrounded;
 //   * O = vs * (P8 V8) / l is written as bfloat16, L as float32.
 // Layouts: S^T = K Q^T with the query on the lane. MFMA row m of key block kb reads key
 // 32 ((m >> 2) & 1) + 16 kb + 4 (m >> 3) + (m & 3), so the 16 accumulators of lane half h
@@ -19,8 +20,9 @@
 // exactly the 32 consecutive keys that lane half h supplies as the B operand of the
 // 64-key P V product. V^T operands are read with ds_read_b64_tr_b8 (each lane of a
 // 16-lane group receives one column of 8 rows). Tiles are staged through registers, the
-// next tile's loads in flight while the current one is computed. Workgroups of NW waves
-// of 32 queries each (4 by default: three workgroups share a CU).
+// next tile's loads in flight while the current one is computed, into two LDS buffers
+// (one barrier per tile). Workgroups of NW waves of 32 queries each (4 by default: three
+// workgroups share a CU).
 #pragma once
 
 #include "fa_common.hpp"
@@ -43,7 +45,7 @@ struct Fp8Params {
   float c;        // |scale * qs * ks| * log2(e)
   uint32_t qsign; // 0x80808080 when scale * qs * ks < 0 (Q negated on load), else 0
   float vs;       // V scale
-  float tau;      // rescale threshold, log2 units (0: the literal per-block update)
+  float tau;      // rescale threshold, log2 units (at most 2: P' = 2^6 P stays <= 256)
   int xcd_map;
 };
 
@@ -71,8 +73,8 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   constexpr int TOT = BC * CPR;                               // chunks per tile and tensor
   constexpr int PER = (TOT + NW * 64 - 1) / (NW * 64);        // chunks per thread per tile
   static_assert(D == 64 || D == 128, "head dims");
-  __shared__ __attribute__((aligned(1024))) u32x4_t ks[BC * CPR];
-  __shared__ __attribute__((aligned(1024))) u32x4_t vs[BC * CPR];
+  __shared__ __attribute__((aligned(1024))) u32x4_t ks2[2][BC * CPR];
+  __shared__ __attribute__((aligned(1024))) u32x4_t vs2[2][BC * CPR];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -127,7 +129,7 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   // LDS read addresses. K: block kb, MFMA row m = l32 -> key row krow(kb); the chunks
   // 4 t + 2 hh and 4 t + 2 hh + 1 (d = 64 t + 32 hh .. + 31).
   auto krow = [&](int kb) { return 32 * ((l32 >> 2) & 1) + 16 * kb + 4 * (l32 >> 3) + (l32 & 3); };
-  auto k_op = [&](int kb, int t) {
+  auto k_op = [&](const u32x4_t* ks, int kb, int t) {
     const int row = krow(kb);
     const u32x4_t a = ks[row * CPR + ((4 * t + 2 * hh) ^ swz8_k<D>(row))];
     const u32x4_t b = ks[row * CPR + ((4 * t + 2 * hh + 1) ^ swz8_k<D>(row))];
@@ -138,7 +140,7 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   // 32 (g16 >> 1) + 8 j .. + 7 for j = 0..3). In the group, lane (t8, u2) supplies row
   // 32 (g16 >> 1) + 8 j + t8, bytes 8 u2 .. 8 u2 + 7 of chunk 2 db + (g16 & 1).
   const int g16 = lane >> 4, t8 = (lane & 15) >> 1, u2 = lane & 1;
-  auto v_op = [&](int db) {
+  auto v_op = [&](const u32x4_t* vs, int db) {
     i32x8_t r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -155,26 +157,25 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   // staging: thread chunk t -> row (tid + 64 NW t) / CPR, chunk tid % CPR (threads past
   // the tile's chunks idle)
   u32x4_t kn[PER], vn[PER];
+  // Rows past N repeat row N - 1 (finite; their scores are masked to -inf, so their
+  // probabilities are 0); no select touches the loaded values before the store.
   auto fetch = [&](int j) {
     const int k0 = j * BC;
 #pragma unroll
     for (int t = 0; t < PER; ++t) {
-      const int idx = tid + NW * 64 * t, row = idx / CPR, ch = idx % CPR;
-      kn[t] = u32x4_t{0u, 0u, 0u, 0u};
-      vn[t] = u32x4_t{0u, 0u, 0u, 0u};
-      if (idx < TOT && k0 + row < N) {
-        kn[t] = *reinterpret_cast<const u32x4_t*>(kg + (size_t)(k0 + row) * D + ch * 16);
-        vn[t] = *reinterpret_cast<const u32x4_t*>(vg + (size_t)(k0 + row) * D + ch * 16);
-      }
+      const int idx = min(tid + NW * 64 * t, TOT - 1), row = idx / CPR, ch = idx % CPR;
+      const size_t off = (size_t)min(k0 + row, N - 1) * D + ch * 16;
+      kn[t] = *reinterpret_cast<const u32x4_t*>(kg + off);
+      vn[t] = *reinterpret_cast<const u32x4_t*>(vg + off);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int t = 0; t < PER; ++t) {
       const int idx = tid + NW * 64 * t, row = idx / CPR, ch = idx % CPR;
       if (idx < TOT) {
-        ks[row * CPR + (ch ^ swz8_k<D>(row))] = kn[t];
-        vs[row * CPR + (ch ^ swz8_v<D>(row))] = vn[t];
+        ks2[buf][row * CPR + (ch ^ swz8_k<D>(row))] = kn[t];
+        vs2[buf][row * CPR + (ch ^ swz8_v<D>(row))] = vn[t];
       }
     }
   };
@@ -187,77 +188,85 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   float ms = -__builtin_inff(), l_part = 0.f;
   const float c = p.c;
 
+  // Tile t lives in buffer t % 2. Iteration j computes tile j, stores tile j+1 (already
+  // in registers) into the other buffer, whose last readers (tile j-1) all passed the
+  // previous barrier, then waits at one barrier and issues the loads of tile j+2.
   fetch(0);
+  stage(0);
+  __syncthreads();
+  if (n_kt > 1) fetch(1);
   for (int j = 0; j < n_kt; ++j) {
     const int k0 = j * BC;
-    __syncthreads();  // the previous tile's reads are done
-    stage();
-    __syncthreads();
-    if (j + 1 < n_kt) fetch(j + 1);
-    if (!wave_live || j >= w_kt) continue;
-    // S^T of the 64 keys (two 32-key blocks)
-    f32x16_t s[2];
+    const u32x4_t* ks = ks2[j & 1];
+    const u32x4_t* vs = vs2[j & 1];
+    if (wave_live && j < w_kt) {
+      // S^T of the 64 keys (two 32-key blocks)
+      f32x16_t s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_op(kb, t), qf[t], s[kb], 0, 0, 0,
-                                                                0, 0, 0);
-    }
-    // masks on the tiles that reach past N or cross the diagonal
-    if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > wq0)) {
+        for (int t = 0; t < NT; ++t)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(k_op(ks, kb, t), qf[t], s[kb], 0, 0, 0,
+                                                                  0, 0, 0);
+      }
+      // masks on the tiles that reach past N or cross the diagonal
+      if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > wq0)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * hh + 16 * kb + r;
+            if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -__builtin_inff();
+          }
+      }
+      // running max (raw dot units); rescale only when some row rose by more than tau
+      float mx = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * hh + 16 * kb + r;
-          if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -__builtin_inff();
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+      mx = xhalf_max(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > ms + p.tau) != 0) {
+        const float ms_new = __builtin_fmaxf(ms, mx);
+        const float alpha = __builtin_amdgcn_exp2f(ms - ms_new);  // 0 on the first tile
+        ms = ms_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      // P' = 2^6 exp2(s c - m) <= 256: fp32 sum, e4m3 bytes for the P V product (key
+      // 32 hh + 16 kb + r is byte 16 kb + r of the lane's operand)
+      i32x8_t pb;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float pv[4];
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            pv[y] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w + y], c, 6.0f - ms));
+            l_part += pv[y];
+          }
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
+          pb[4 * kb + w] = word;
         }
-    }
-    // running max (raw dot units); rescale only when some row rose by more than tau
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
-    mx = xhalf_max(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > ms + p.tau) != 0) {
-      const float ms_new = __builtin_fmaxf(ms, mx);
-      const float alpha = __builtin_amdgcn_exp2f(ms - ms_new);  // 0 on the first tile
-      ms = ms_new;
-      l_part *= alpha;
+      // O^T += V^T P^T over the 64 keys
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_op(vs, db), pb, oacc[db], 0, 0, 0,
+                                                                   0, 0, 0);
     }
-    // P' = 2^8 exp2(s c - m) <= 256: fp32 sum, e4m3 bytes for the P V product (key
-    // 32 hh + 16 kb + r is byte 16 kb + r of the lane's operand)
-    i32x8_t pb;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float pv[4];
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          pv[y] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w + y], c, 8.0f - ms));
-          l_part += pv[y];
-        }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], word, true);
-        pb[4 * kb + w] = word;
-      }
-    // O^T += V^T P^T over the 64 keys
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_op(db), pb, oacc[db], 0, 0, 0, 0,
-                                                                 0, 0);
+    if (j + 1 < n_kt) stage((j + 1) & 1);
+    __syncthreads();
+    if (j + 2 < n_kt) fetch(j + 2);
   }
 
-  // epilogue: O = vs * O~ / l (bfloat16; the 2^8 cancels), L = (m - 8 + log2 l) ln 2
+  // epilogue: O = vs * O~ / l (bfloat16; the 2^6 cancels), L = (m - 6 + log2 l) ln 2
   if (!wave_live || qi >= N) return;
   const float l_tot = xhalf_sum(l_part);
   const float mul = p.vs / l_tot;
@@ -273,7 +282,7 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
                   Elt<true>::pack(a[4 * g + 2] * mul, a[4 * g + 3] * mul)};
     }
   if (hh == 0)
-    p.lse[(size_t)bh * N + qi] = (ms - 8.0f + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+    p.lse[(size_t)bh * N + qi] = (ms - 6.0f + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
 }
 
 }  // namespace fa
