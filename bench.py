@@ -238,8 +238,10 @@ def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands, 
     w = workloads.get(workload)
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
-    key = "fa_fwd_fa1" if path == "fa1" else "fa_fwd_wide"
-    fa_name = next(k for k in fetch if key in k)
+    if path == "fa1":
+        fa_name = next(k for k in fetch if "fa_fwd_fa1" in k)
+    else:  # the 16-bit forward kernel of this workload (wide, 32-query or generic)
+        fa_name = next(k for k in fetch if "fa_fwd" in k and "fa1" not in k and "fp8" not in k)
     copy_name = next(k for k in fetch if "MulFunctor" in k)
     copy_kib = copy_mib * 1024.0
     f_scale = copy_kib / fetch[copy_name]
