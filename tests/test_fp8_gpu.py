@@ -185,3 +185,53 @@ def test_fp8_raw_abi_errors():
     assert fa.fa_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, 1, 2, 100, 64, 0.1, 0, None) == fa.FA_OK
     torch.cuda.synchronize()
     del args
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_accumulation_model(causal):
+    """The score error term of the bar, observed through the C ABI. With one key, L is the
+    score itself (L = S_00 = scale qs ks <q8, k8>), so L shows how the 8-bit matrix core
+    sums the products: those of each group of 8 consecutive head dims are aligned to the
+    group's largest and truncated toward zero at 2^-13 of it. A group holding 256 * 256
+    and seven 1 * 1 products sums to 2^16 (the exact 2^16 + 7 loses the ones), while
+    products of equal size sum exactly."""
+    d = 64
+    ONE, P256 = 0x38, 0x78  # E4M3 codes of 1.0 and 256.0
+    o = torch.empty((1, 1, 1, d), dtype=torch.bfloat16, device=DEV)
+    v8 = torch.full((1, 1, 1, d), ONE, dtype=torch.uint8, device=DEV)
+    cases = []
+    # (q codes, k codes, the hardware dot product, the exact one)
+    q = np.zeros(d, np.uint8); k = np.zeros(d, np.uint8)
+    q[:8] = ONE; k[:8] = ONE; q[0] = k[0] = P256
+    cases.append((q.copy(), k.copy(), 65536.0, 65536.0 + 7))
+    q = np.zeros(d, np.uint8); k = np.zeros(d, np.uint8)
+    q[:8] = ONE; k[:8] = ONE
+    q[8:16] = ONE; k[8:16] = ONE                 # 16 products of 1 in two groups: exact
+    cases.append((q.copy(), k.copy(), 16.0, 16.0))
+    for qc, kc, hw, exact in cases:
+        q8 = torch.from_numpy(qc.reshape(1, 1, 1, d)).to(DEV)
+        k8 = torch.from_numpy(kc.reshape(1, 1, 1, d)).to(DEV)
+        lse = torch.empty((1, 1, 1), dtype=torch.float32, device=DEV)
+        sc = 1.0 / hw  # scale * qs * ks: the hardware's score becomes 1
+        st = fa.fa_fwd_fp8(q8, k8, v8, 1.0, 1.0, 1.0, o, lse, 1, 1, 1, d, sc, int(causal), None)
+        assert st == fa.FA_OK
+        torch.cuda.synchronize()
+        L = float(lse.item())
+        # oracle on the decoded codes: the exact score
+        O_ref, L_ref = oracle.attention_fp8(qc.reshape(1, 1, 1, d), kc.reshape(1, 1, 1, d),
+                                            np.full((1, 1, 1, d), ONE, np.uint8), 1.0, 1.0,
+                                            1.0, sc, bool(causal))
+        rec = {"case": f"fp8/accumulation/{hw:g}", "L": L, "L_exact": float(L_ref[0, 0, 0]),
+               "model": 1.0}
+        _REPORT.append(rec)
+        print(json.dumps(rec), flush=True)
+        assert abs(L - 1.0) <= 2e-6, rec                       # the truncation model (fp32 path)
+        if hw != exact:
+            assert abs(L - exact / hw) >= 5e-5, rec            # and not the exact sum
+        assert abs(float(L_ref[0, 0, 0]) - exact / hw) <= 1e-12  # the oracle's exact score
+        # the bar's score term covers the difference
+        ds = 7 * 2.0 ** -13 * sc * sum(
+            max(abs(oracle.decode_e4m3(qc[i]) * oracle.decode_e4m3(kc[i])) for i in range(g, g + 8))
+            for g in range(0, d, 8))
+        assert abs(L - float(L_ref[0, 0, 0])) <= ds + 2e-6
+        assert torch.equal(o.float().cpu(), torch.ones_like(o, dtype=torch.float32).cpu())
