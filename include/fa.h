@@ -12,11 +12,13 @@
  *       우회하다" (the chapter's second page)
  *
  * The library never allocates device memory, keeps no pointer after a call returns
- * and needs no workspace (the O(N) extra memory of the [P1] "정리" comparison table
- * is the L output itself). Its only global state is the compute-unit count of each
- * device, read once per device (std::call_once) and immutable afterwards; it only
- * steers which of the call's own Q and K rows a workgroup pre-loads into the L2 (a
- * performance hint, never a correctness input). Calls are reentrant and
+ * and needs no workspace except where an entry point takes one from the caller (the O(N)
+ * extra memory of the [P1] "정리" comparison table is the L output itself). Its only
+ * global state is the compute-unit count and the LDS size per compute unit of each
+ * device, read once per device (std::call_once) and immutable afterwards; they only
+ * steer which of the call's own Q and K rows a workgroup pre-loads into the L2 and how
+ * many 8-bit workgroups share a compute unit (performance hints, never correctness
+ * inputs). Calls are reentrant and
  * thread-safe. No C++ exception crosses this boundary.
  */
 #ifndef FA_H_

@@ -337,12 +337,14 @@ constexpr float kFp8Tau = 2.0f;  // probabilities <= 4 before the 2^6 scale (<= 
 // The 1.15 is the measured throughput gain of the third resident workgroup.
 size_t fp8_lds_cap(int grid, bool causal, size_t static_lds) {
   const int cus = fa_host::cu_count();
-  if (causal || cus <= 0 || FA_FP8_NW != 4) return 0;
+  const size_t per_cu = fa_host::lds_per_cu();
+  if (causal || cus <= 0 || per_cu == 0 || FA_FP8_NW != 4) return 0;
   const double r3 = std::ceil(grid / (3.0 * cus)) * 3.0 / 1.15;
   const double r2 = std::ceil(grid / (2.0 * cus)) * 2.0;
   if (r2 >= r3) return 0;
-  const size_t per_cu = 160 * 1024, want = per_cu / 2 - 1024;  // two fit, three do not
-  return want > static_lds ? want - static_lds : 0;
+  const size_t want = per_cu / 2 - 1024;  // two workgroups fit in a CU's LDS, three do not
+  if (3 * want <= per_cu || want <= static_lds) return 0;
+  return want - static_lds;
 }
 
 template <int D, bool CAUSAL>

@@ -25,6 +25,22 @@ inline int cu_count() {
   return count[dev];
 }
 
+// LDS bytes per CU of the current device, read once per device (0 if unknown).
+inline size_t lds_per_cu() {
+  static std::once_flag once[64];
+  static size_t bytes[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::call_once(once[dev], [dev]() {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+        hipSuccess)
+      n = 0;
+    bytes[dev] = n > 0 ? static_cast<size_t>(n) : 0;
+  });
+  return bytes[dev];
+}
+
 inline bool ranges_overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a);
   const uintptr_t b0 = reinterpret_cast<uintptr_t>(b);

@@ -111,7 +111,7 @@ def test_variant_full_ai2048_sampled(path):
     _check(f"{path}/ai2048/sampled", "bf16", og, lg, O, L)
 
 
-def test_variants_agree_with_fa2_bitwise_free():
+def test_variants_agree_with_fa2():
     """The three loop organisations give the same O and L up to rounding on one input."""
     w = Workload("agree", 2, 4, 900, 128, "bf16", True, seed=8300)
     q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
