@@ -164,7 +164,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float
 /*
  * fa_fwd_splitkv — the operation of fa_fwd_ex (same outputs, up to rounding), with the
  * keys of every head split into ranges that separate workgroups process, for shapes
- * whose B * H * ceil(N / 256) query tiles are too few to fill the GPU (few heads,
+ * whose B * H * ceil(N / 128) query tiles are too few to fill the GPU (few heads,
  * moderate N).
  *
  * Each split runs the FA2-order forward over its key range and leaves its normalized
@@ -175,7 +175,8 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float
  * of two).
  *
  * n_splits in [1, FA_MAX_SPLITS] is an upper bound: the keys per split are
- * ceil(N / n_splits) rounded up to a multiple of 256, so fewer splits may run. Under
+ * ceil(N / n_splits) rounded up to a multiple of 128 (the query tile), so fewer splits
+ * may run. Under
  * the causal mask a split that lies wholly after a query tile contributes L_s = -inf.
  * d must be 64 or 128 (FA_ERR_UNSUPPORTED) and scale nonzero (FA_ERR_SHAPE).
  *

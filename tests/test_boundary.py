@@ -205,10 +205,13 @@ def test_workspace_pass_validation(L, no_gpu, which):
         assert fa.fa_fwd_splitkv_workspace_size(1, 1, 100, 64, fa.FA_MAX_SPLITS + 1) == 0
         assert call(ns=0, nbytes=1 << 30) == fa.FA_ERR_SHAPE
         assert call(ns=fa.FA_MAX_SPLITS + 1, nbytes=1 << 30) == fa.FA_ERR_SHAPE
-        # keys per split are a multiple of 256: N = 1000 with 8 requested splits runs 4
-        per_split = 1000 * 64 * 4 + 1000 * 4
-        assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) <= 4 * per_split + 512
-        assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) >= 4 * per_split
+        # keys per split are a multiple of the 128-query tile: N = 300 with 8 requested
+        # splits runs 3 (128 keys each), N = 1000 with 8 runs 8
+        per_split = lambda n: n * 64 * 4 + n * 4  # noqa: E731
+        assert 3 * per_split(300) <= fa.fa_fwd_splitkv_workspace_size(1, 1, 300, 64, 8) \
+            <= 3 * per_split(300) + 512
+        assert 8 * per_split(1000) <= fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) \
+            <= 8 * per_split(1000) + 512
     assert fa.fa_last_hip_error() == 0
 
 
