@@ -94,31 +94,6 @@ struct BwdTile {
   }
 };
 
-// Workgroup -> (head, tile rank). When B*H is a multiple of 8 the tiles of one head
-// stay on one XCD (workgroups are dispatched round-robin over the 8 XCDs), so its
-// rows are fetched into one L2 only. Under the causal mask rank 0 is the tile with the
-// most work and ranks are issued in increasing order over all heads, so the short
-// tiles fill the tail of the grid.
-template <bool CAUSAL>
-__device__ __forceinline__ void bwd_decode(int bid, int BH, int n_t, int& bh, int& rank) {
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, s = bid >> 3, hpx = BH >> 3;
-    if (CAUSAL) {
-      rank = s / hpx;
-      bh = (s % hpx) * 8 + xcd;
-    } else {
-      bh = xcd * hpx + s / n_t;
-      rank = s % n_t;
-    }
-  } else if (CAUSAL) {
-    rank = bid / BH;
-    bh = bid % BH;
-  } else {
-    bh = bid / n_t;
-    rank = bid % n_t;
-  }
-}
-
 // Per-lane byte offsets of the transposed operand reads (A = M^T over 16 rows of a
 // staged tile, one 32-column block db): half h covers rows 4h .. 4h+3 of each 8-row
 // group. The chunk swizzle depends on the row modulo 16 only, which a multiple of
@@ -182,7 +157,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
   const int N = p.N;
   const int n_qt = (N + BQ - 1) / BQ;
   int bh, rank;
-  bwd_decode<CAUSAL>(blockIdx.x, p.BH, n_qt, bh, rank);
+  tile_order<CAUSAL>(blockIdx.x, p.BH, n_qt, bh, rank);
   const int qt = CAUSAL ? n_qt - 1 - rank : rank;  // the last query tile sees the most keys
   const size_t head = (size_t)bh * (size_t)N * D;
   const int q0 = qt * BQ, qi = q0 + wid * 32 + l32;
@@ -282,7 +257,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
   const int N = p.N;
   const int n_kt = (N + BKV - 1) / BKV;
   int bh, kt;
-  bwd_decode<CAUSAL>(blockIdx.x, p.BH, n_kt, bh, kt);  // the first key tile sees the most queries
+  tile_order<CAUSAL>(blockIdx.x, p.BH, n_kt, bh, kt);  // the first key tile sees the most queries
   const size_t head = (size_t)bh * (size_t)N * D;
   const int k0 = kt * BKV, kj = k0 + wid * 32 + l32;
   const bool wave_live = k0 + wid * 32 < N;

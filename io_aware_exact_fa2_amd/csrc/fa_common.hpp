@@ -27,7 +27,6 @@ struct Params {
   int n_qt;       // query tiles per head
   float c;        // |scale| * log2(e)
   uint32_t qsign; // 0x80008000 when scale < 0: Q is negated on load (exact), else 0
-  int xcd_map;    // 1 when BH % 8 == 0: the heads of one XCD stay on it
   float tau;      // rescale threshold in log2 units (fast kernel; 0: every tile)
   int next_stride;  // > 0: workgroup b warms the L2 with the Q tile of workgroup b + next_stride
   // split-KV partial pass: keys [s * split_keys, (s + 1) * split_keys) for split s; the
@@ -126,28 +125,38 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)pr[0]) + __builtin_bit_cast(float, (uint32_t)pr[1]);
 }
 
-// Workgroup -> (head, query tile). Workgroups are dispatched round-robin over the
-// 8 XCDs (bid % 8). When the head count allows, all query tiles of a head run on
-// one XCD so its K and V stay in that XCD's L2; causal grids issue the longest
-// (last) query tiles first so the short ones fill the tail.
+// Workgroup -> (head, tile rank), for a grid of BH * n_t workgroups. Workgroups are
+// dispatched round-robin over the 8 XCDs (bid % 8). When BH is a multiple of 8 all tiles
+// of a head run on one XCD, so its rows are fetched into that XCD's L2 only. Under the
+// causal mask ranks are issued in increasing order over all heads (rank 0 = the tile
+// with the most work, which the caller maps to its tile index), so the short tiles fill
+// the tail of the grid.
 template <bool CAUSAL>
-__device__ __forceinline__ void decode_tile(const Params& p, int bid, int& bh, int& qt) {
-  if (p.xcd_map) {
-    const int xcd = bid & 7, s = bid >> 3, hpx = p.BH >> 3;
+__device__ __forceinline__ void tile_order(int bid, int BH, int n_t, int& bh, int& rank) {
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, s = bid >> 3, hpx = BH >> 3;
     if (CAUSAL) {
-      qt = p.n_qt - 1 - s / hpx;
+      rank = s / hpx;
       bh = (s % hpx) * 8 + xcd;
     } else {
-      bh = xcd * hpx + s / p.n_qt;
-      qt = s % p.n_qt;
+      bh = xcd * hpx + s / n_t;
+      rank = s % n_t;
     }
   } else if (CAUSAL) {
-    qt = p.n_qt - 1 - bid / p.BH;
-    bh = bid % p.BH;
+    rank = bid / BH;
+    bh = bid % BH;
   } else {
-    bh = bid / p.n_qt;
-    qt = bid % p.n_qt;
+    bh = bid / n_t;
+    rank = bid % n_t;
   }
+}
+
+// Forward kernels: the last query tile sees the most keys under the causal mask.
+template <bool CAUSAL>
+__device__ __forceinline__ void decode_tile(const Params& p, int bid, int& bh, int& qt) {
+  int rank;
+  tile_order<CAUSAL>(bid, p.BH, p.n_qt, bh, rank);
+  qt = CAUSAL ? p.n_qt - 1 - rank : rank;
 }
 
 }  // namespace fa

@@ -141,7 +141,6 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   p.n_qt = 0;  // set per launch shape
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
-  p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
   p.tau = tau;
   p.next_stride = 0;
   p.split_keys = 0;
@@ -264,7 +263,6 @@ int fa_splitkv_impl(const void* q, const void* k, const void* v, void* o, float*
   p.BH = B * H;
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
-  p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
   p.tau = FA_DEFAULT_RESCALE_LOG2;
   p.next_stride = 0;
   p.split_keys = keys;
@@ -398,7 +396,6 @@ int fa_fp8_impl(const void* q, const void* k, const void* v, float q_scale, floa
   p.qsign = cs < 0.0 ? 0x80808080u : 0u;
   p.vs = v_scale;
   p.tau = kFp8Tau;
-  p.xcd_map = (p.BH % 8) == 0 ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool cz = causal != 0;
   hipError_t e;

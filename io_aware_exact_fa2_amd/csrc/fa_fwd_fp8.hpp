@@ -46,7 +46,6 @@ struct Fp8Params {
   uint32_t qsign; // 0x80808080 when scale * qs * ks < 0 (Q negated on load), else 0
   float vs;       // V scale
   float tau;      // rescale threshold, log2 units (at most 2: P' = 2^6 P stays <= 256)
-  int xcd_map;
 };
 
 // Chunk swizzles (16-byte chunks, rows of D bytes). K rows are read as MFMA row operands
@@ -80,26 +79,8 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
   int bh, qt;
-  {
-    // same map as the 16-bit kernels: heads of one XCD stay on it, causal longest first
-    const int bid = blockIdx.x;
-    if (p.xcd_map) {
-      const int xcd = bid & 7, s = bid >> 3, hpx = p.BH >> 3;
-      if (CAUSAL) {
-        qt = p.n_qt - 1 - s / hpx;
-        bh = (s % hpx) * 8 + xcd;
-      } else {
-        bh = xcd * hpx + s / p.n_qt;
-        qt = s % p.n_qt;
-      }
-    } else if (CAUSAL) {
-      qt = p.n_qt - 1 - bid / p.BH;
-      bh = bid % p.BH;
-    } else {
-      bh = bid / p.n_qt;
-      qt = bid % p.n_qt;
-    }
-  }
+  tile_order<CAUSAL>(blockIdx.x, p.BH, p.n_qt, bh, qt);
+  if (CAUSAL) qt = p.n_qt - 1 - qt;  // the last query tile sees the most keys
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint8_t* __restrict__ kg = p.k + head;
   const uint8_t* __restrict__ vg = p.v + head;
