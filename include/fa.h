@@ -276,6 +276,14 @@ int fa_bwd_fp16(const void* q, const void* k, const void* v, const void* o, cons
  */
 int fa_fwd_supported(int d, int dtype, int causal);
 
+/*
+ * fa_device_supported — 1 if HIP device `device` is one this library has code for
+ * (a gfx950 GPU, e.g. MI355X), else 0 (also when the device does not exist or the HIP
+ * runtime reports an error). The GPU half of the support question of [P3] "실제로
+ * 적용한다면 먼저 재볼 것". Reads the device properties; launches nothing.
+ */
+int fa_device_supported(int device);
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* fa_strerror(int status);
 

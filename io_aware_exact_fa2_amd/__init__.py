@@ -23,7 +23,7 @@ __all__ = [
     "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
     "fa_bwd", "fa_bwd_fp16", "backward", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
     "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "forward_splitkv", "forward_fa1", "FA_MAX_SPLITS",
-    "fa_fwd_fp8", "forward_fp8",
+    "fa_fwd_fp8", "forward_fp8", "fa_device_supported",
     "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
 ]
@@ -40,6 +40,7 @@ FA_DTYPE_FP16 = 1
 
 EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
            "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
+           "fa_device_supported",
            "fa_strerror", "fa_last_hip_error", "fa_version")
 FA_MAX_SPLITS = 64
 FA_DEFAULT_RESCALE_LOG2 = 8.0
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         fn.restype = i
+    L.fa_device_supported.argtypes = [i]
+    L.fa_device_supported.restype = i
     L.fa_fwd_supported.argtypes = [i, i, i]
     L.fa_fwd_supported.restype = i
     L.fa_strerror.argtypes = [i]
@@ -186,6 +189,11 @@ def fa_bwd_fp16(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
     return lib().fa_bwd_fp16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
                              int(causal), _stream(stream))
+
+
+def fa_device_supported(device: int = 0) -> int:
+    """C ``fa_device_supported``: 1 for a gfx950 device, else 0."""
+    return lib().fa_device_supported(int(device))
 
 
 def fa_fwd_supported(d: int, dtype: int, causal: int) -> int:

@@ -480,6 +480,20 @@ int fa_fwd_supported(int d, int dtype, int causal) {
   return 1;
 }
 
+int fa_device_supported(int device) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) {
+    (void)hipGetLastError();  // leave no sticky error behind
+    return 0;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";

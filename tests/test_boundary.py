@@ -59,6 +59,13 @@ def test_strerror_and_version(L):
     assert fa.fa_last_hip_error() == 0
 
 
+def test_device_query_without_a_gpu(L, no_gpu):
+    """On a host without a GPU no device is supported, and the query leaves no error."""
+    assert fa.fa_device_supported(0) == 0
+    assert fa.fa_device_supported(-1) == 0
+    assert fa.fa_last_hip_error() == 0
+
+
 def test_supported_query(L):
     for d in (1, 4, 63, 64, 65, 127, 128):
         for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16):

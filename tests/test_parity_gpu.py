@@ -347,6 +347,13 @@ def test_side_stream():
     _check("side_stream", "bf16", to_f64(o), to_f64(lse), O, L)
 
 
+def test_device_supported():
+    """The MI355X this runs on is a gfx950 device; a device index past the last is not."""
+    assert fa.fa_device_supported(torch.cuda.current_device()) == 1
+    assert fa.fa_device_supported(torch.cuda.device_count()) == 0
+    assert fa.fa_device_supported(-1) == 0
+
+
 def test_raw_abi_call_matches_forward():
     w = workloads.get("tiny")
     q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
