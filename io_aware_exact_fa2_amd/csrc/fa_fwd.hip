@@ -509,6 +509,8 @@ const char* fa_strerror(int status) {
 
 int fa_last_hip_error(void) { return g_last_hip_error; }
 
-const char* fa_version(void) { return "fa355 0.1.0 (gfx950, FA2 forward)"; }
+const char* fa_version(void) {
+  return "fa355 0.2.0 (gfx950: FA2-order forward bf16/fp16/fp8, backward, split-KV, FA1 ablation)";
+}
 
 }  // extern "C"

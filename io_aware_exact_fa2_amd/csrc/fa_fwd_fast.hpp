@@ -8,7 +8,9 @@
 // inner loop, each row keeps its running max and sum on chip, rescales the
 // unnormalised output by alpha = exp(m_old - m_new) only, and divides once at the
 // end (the section's per-block update and epilogue equations). Waves own disjoint
-// query rows (split-Q), so no cross-wave merge exists.
+// query rows (split-Q), so no cross-wave merge exists. With SPLIT, workgroup (s, head,
+// query block) covers only the keys of split s and writes its normalized partial O and
+// partial L in float32 for the split-KV merge (fa_fwd_split.hpp).
 //
 // gfx950 mapping:
 //   * K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register
