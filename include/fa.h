@@ -241,7 +241,10 @@ size_t fa_fwd_fa1_workspace_size(int B, int H, int N, int d);
  *            values give the gradients of a different function (unspecified).
  *   dout     dLoss/dO, [B, H, N, d] bfloat16 (read only), 16-byte aligned.
  *   dq, dk, dv  outputs, [B, H, N, d] bfloat16, written with round-to-nearest-
- *            even; 16-byte aligned; each written by exactly one workgroup.
+ *            even; 16-byte aligned; each element written by exactly one workgroup.
+ *            Between the call's kernels dq's memory also holds D (B*H*N float32):
+ *            computed once there before the dK/dV kernel reads it, then overwritten
+ *            by dQ, so on completion dq holds dQ. Nothing else is written.
  *   B, H, N  each >= 1.
  *   d        64 or 128 (FA_ERR_UNSUPPORTED otherwise).
  *   scale, causal  as passed to fa_fwd.
@@ -253,7 +256,7 @@ size_t fa_fwd_fa1_workspace_size(int B, int H, int N, int d);
  *
  * Errors and asynchrony: as fa_fwd (validation on the host before any HIP call;
  * FA_ERR_HIP with fa_last_hip_error() when a launch is refused; the call only
- * enqueues two kernels on `stream`).
+ * enqueues three kernels on `stream`, in order: D, then dK and dV, then dQ).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,

@@ -47,15 +47,23 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
+// Three launches in stream order: D into dq's memory, dK and dV (reading D), then dQ
+// (overwriting that memory; it computes D for its own rows).
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_bwd(const fa::BwdParams& p, hipStream_t s) {
   const int tiles = (p.N + kBwdRows - 1) / kBwdRows;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
-                     s, p);
-  const hipError_t e = hipGetLastError();
+  const long long rows = static_cast<long long>(p.BH) * p.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<BF16, D>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)),
+                     dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256),
                      0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
+                     s, p);
   return hipGetLastError();
 }
 
@@ -75,6 +83,7 @@ int fa_bwd_impl(const void* q, const void* k, const void* v, const void* o, cons
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
+  p.delta = static_cast<float*>(dq);  // B*H*N floats fit in dq's B*H*N*d*2 bytes (d >= 64)
   p.N = N;
   p.BH = B * H;
   p.scale = scale;

@@ -17,7 +17,9 @@
 //   * fa_bwd_dkdv_kernel: one workgroup per 128 keys (32 per wave) walks the query
 //     tiles, recomputing S and dP with the key on the lane, and accumulates
 //     dV^T = dO^T P and dK^T = Q^T dS.
-// D is recomputed from dO and O where it is needed. All products run on
+// D is computed once per row from dO and O (fa_bwd_delta_kernel, into the dQ output's
+// memory before dQ is written) for the dK/dV kernel; the dQ kernel, which runs last,
+// computes it for its own rows. All products run on
 // v_mfma_f32_32x32x16_{bf16,f16}; an accumulator becomes a 16-bit B operand of the next
 // product by the row permutation of the forward kernels (bits 2 and 3 of the MFMA row
 // swapped). Tiles are staged in LDS through registers (the next tile's loads are in
@@ -47,6 +49,7 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
+  float* delta;  // [BH, N] D_i = rowsum(dO * O); lives in dq's memory until dQ is written
   int N;
   int BH;
   float scale;  // signed
@@ -144,6 +147,28 @@ __device__ __forceinline__ void bwd_store_rows(uint16_t* dst, const f32x16_t (&a
       const uint32_t w1 = E::pack(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul);
       *reinterpret_cast<u32x2_t*>(r + dcol) = u32x2_t{w0, w1};
     }
+}
+
+// ---- D = rowsum(dO * O): one pass, CPR threads per row ---------------------------------
+// Written to p.delta (the dQ output's memory, as float32) for the dK/dV kernel, which
+// would otherwise recompute it for every key tile; the dQ kernel runs after it and
+// computes D for its own rows.
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p) {
+  using E = Elt<BF16>;
+  constexpr int CPR = D / 8, RPB = 256 / CPR;  // chunks per row, rows per workgroup
+  const long long rows = (long long)p.BH * p.N;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / CPR;
+  const int ch = threadIdx.x % CPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4_t a = ld16(p.dout + row * D + ch * 8), b = ld16(p.o + row * D + ch * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = E::dot2(a[w], b[w], acc);
+  }
+#pragma unroll
+  for (int m = 1; m < CPR; m <<= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && ch == 0) p.delta[row] = acc;
 }
 
 // ---- dQ: one workgroup per 128 query rows -------------------------------------------
@@ -291,18 +316,19 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) troff[db][h] = bwd_tr_off<D>(lane, db, h);
 
-  // Q, dO and O of the next query tile, and its L, in flight while a tile is computed
+  // Q and dO of the next query tile, and L and D of its rows (thread t < BQ: row t), in
+  // flight while a tile is computed. D comes from fa_bwd_delta_kernel (one pass over dO
+  // and O) instead of being recomputed here for every key tile.
   using Tile = BwdTile<D, BQ, NW * 64>;
-  Tile qn, don, on;
-  float ln[Tile::PER];
+  Tile qn, don;
+  float ln = 0.f, dn = 0.f;
   auto fetch = [&](int qb0) {
     qn.load(p.q + head, qb0, N, tid);
     don.load(p.dout + head, qb0, N, tid);
-    on.load(p.o + head, qb0, N, tid);
-#pragma unroll
-    for (int t = 0; t < Tile::PER; ++t) {
-      const int q = qb0 + Tile::row_of(tid, t);
-      ln[t] = p.lse[(size_t)bh * N + min(q, N - 1)];  // rows past N: masked
+    if (tid < BQ) {
+      const size_t r = (size_t)bh * N + min(qb0 + tid, N - 1);  // rows past N: masked
+      ln = p.lse[r];
+      dn = p.delta[r];
     }
   };
   fetch(i0 * BQ);
@@ -311,20 +337,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
     __syncthreads();  // the previous tile's reads are done
     qn.store(qs, tid);
     don.store(dos, tid);
-    // D_i = rowsum(dO * O) and L_i of the tile's rows: the CPR threads holding one row
-    // (consecutive lanes) reduce their chunks' dot products
-#pragma unroll
-    for (int t = 0; t < Tile::PER; ++t) {
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc = E::dot2(don.x[t][w], on.x[t][w], acc);
-#pragma unroll
-      for (int m = 1; m < CPR; m <<= 1) acc += __shfl_xor(acc, m);
-      if (tid % CPR == 0) {
-        const int row = Tile::row_of(tid, t);
-        dsh[row] = acc;
-        lsh[row] = ln[t] * 1.4426950408889634f;
-      }
+    if (tid < BQ) {
+      dsh[tid] = dn;
+      lsh[tid] = ln * 1.4426950408889634f;
     }
     __syncthreads();
     if (i + 1 < n_qt) fetch(qb0 + BQ);
