@@ -29,11 +29,14 @@ CSRC = os.path.join(ROOT, "io_aware_exact_fa2_amd", "csrc")
 
 
 def kernel_hash() -> str:
-    """Short hash of every HIP source file (identifies the kernel a profile was taken on)."""
+    """Short hash of every HIP source file and of the build script that holds the compile
+    options (identifies the kernel a profile was taken on)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    paths = [os.path.join(CSRC, n) for n in sorted(os.listdir(CSRC))]
+    paths.append(os.path.join(ROOT, "io_aware_exact_fa2_amd", "build.py"))
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

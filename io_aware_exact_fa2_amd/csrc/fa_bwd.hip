@@ -1,5 +1,5 @@
 // fa_bwd.hip — host side of the backward entry points declared in include/fa.h:
-// validation (entirely before any HIP call) and the two kernel launches.
+// validation (entirely before any HIP call) and dispatch to the launches of the head dim.
 #include "fa.h"
 #include "fa_bwd.hpp"
 #include "fa_host.hpp"
@@ -9,9 +9,22 @@
 #include <cmath>
 #include <cstdint>
 
+// The launches live in fa_bwd_d64.hip and fa_bwd_d128.hip (one translation unit per
+// head dim, each compiled with its own options); nothing here instantiates them.
+namespace fa {
+extern template hipError_t launch_bwd<true, 64, false>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<true, 64, true>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<false, 64, false>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<false, 64, true>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<true, 128, false>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<true, 128, true>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<false, 128, false>(const BwdParams&, hipStream_t);
+extern template hipError_t launch_bwd<false, 128, true>(const BwdParams&, hipStream_t);
+}  // namespace fa
+
 namespace {
 
-constexpr int kBwdRows = 128;  // query rows per dQ workgroup = keys per dK/dV workgroup
+using fa::kBwdRows;
 
 int validate_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, const void* dq, const void* dk, const void* dv, int B, int H,
@@ -47,26 +60,6 @@ int validate_bwd(const void* q, const void* k, const void* v, const void* o, con
   return FA_OK;
 }
 
-// Three launches in stream order: D into dq's memory, dK and dV (reading D), then dQ
-// (overwriting that memory; it computes D for its own rows).
-template <bool BF16, int D, bool CAUSAL>
-hipError_t launch_bwd(const fa::BwdParams& p, hipStream_t s) {
-  const int tiles = (p.N + kBwdRows - 1) / kBwdRows;
-  const long long rows = static_cast<long long>(p.BH) * p.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((fa::fa_bwd_delta_kernel<BF16, D>), dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)),
-                     dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa::fa_bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256),
-                     0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa::fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
-                     s, p);
-  return hipGetLastError();
-}
-
 template <bool BF16>
 int fa_bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
@@ -91,8 +84,9 @@ int fa_bwd_impl(const void* q, const void* k, const void* v, const void* o, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool cz = causal != 0;
   hipError_t e;
-  if (d == 128) e = cz ? launch_bwd<BF16, 128, true>(p, s) : launch_bwd<BF16, 128, false>(p, s);
-  else e = cz ? launch_bwd<BF16, 64, true>(p, s) : launch_bwd<BF16, 64, false>(p, s);
+  if (d == 128)
+    e = cz ? fa::launch_bwd<BF16, 128, true>(p, s) : fa::launch_bwd<BF16, 128, false>(p, s);
+  else e = cz ? fa::launch_bwd<BF16, 64, true>(p, s) : fa::launch_bwd<BF16, 64, false>(p, s);
   if (e != hipSuccess) {
     fa_host::g_last_hip_error = static_cast<int>(e);
     return FA_ERR_HIP;

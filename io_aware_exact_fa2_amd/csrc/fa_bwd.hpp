@@ -432,4 +432,28 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
   }
 }
 
+// ---- launches ------------------------------------------------------------------------
+constexpr int kBwdRows = 128;  // query rows per dQ workgroup = keys per dK/dV workgroup
+
+// One backward call: three launches in stream order, D into dq's memory, dK and dV
+// (reading D), then dQ (overwriting that memory; it computes D for its own rows).
+// Explicitly instantiated per head dim in fa_bwd_d64.hip and fa_bwd_d128.hip, which
+// are compiled with different code-generation options.
+template <bool BF16, int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  const int tiles = (p.N + kBwdRows - 1) / kBwdRows;
+  const long long rows = static_cast<long long>(p.BH) * p.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((fa_bwd_delta_kernel<BF16, D>),
+                     dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s,
+                     p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace fa

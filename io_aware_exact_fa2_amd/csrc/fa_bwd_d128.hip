@@ -1,0 +1,16 @@
+// fa_bwd_d128.hip — the backward kernels and launches at head dim 128 (bfloat16 and
+// float16, with and without the causal mask), one translation unit per head dim so that
+// each is compiled with its own code-generation options.
+//
+// Compiled with LLVM's iterative ILP machine scheduler (see build.py): at this head dim
+// the dK/dV kernel runs one wave per SIMD with more than 256 registers, and the default
+// scheduler issues each product's LDS operand read just before the product, leaving its
+// latency exposed; the ILP schedule issues the reads earlier.
+#include "fa_bwd.hpp"
+
+namespace fa {
+template hipError_t launch_bwd<true, 128, false>(const BwdParams&, hipStream_t);
+template hipError_t launch_bwd<true, 128, true>(const BwdParams&, hipStream_t);
+template hipError_t launch_bwd<false, 128, false>(const BwdParams&, hipStream_t);
+template hipError_t launch_bwd<false, 128, true>(const BwdParams&, hipStream_t);
+}  // namespace fa
