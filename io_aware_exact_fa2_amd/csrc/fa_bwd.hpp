@@ -9,17 +9,18 @@
 // sum(O * dO)):
 //     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D_i = rowsum(dO * O)_i,
 //     dQ = scale dS K,  dK = scale dS^T Q.
-// Two kernels, so that every output is written by exactly one workgroup (no atomics and
-// no workspace beyond the outputs):
-//   * fa_bwd_dq_kernel: one workgroup per 128 query rows (32 per wave) walks the key
-//     tiles, recomputing S^T and dP^T with the row on the lane (as in the forward), and
-//     accumulates dQ^T = K^T dS^T;
+// Three kernels in stream order, so that every output is written by exactly one
+// workgroup (no atomics and no workspace beyond the outputs):
+//   * fa_bwd_delta_kernel: D once per row from dO and O, into the dQ output's memory
+//     (before dQ is written there);
 //   * fa_bwd_dkdv_kernel: one workgroup per 128 keys (32 per wave) walks the query
 //     tiles, recomputing S and dP with the key on the lane, and accumulates
-//     dV^T = dO^T P and dK^T = Q^T dS.
-// D is computed once per row from dO and O (fa_bwd_delta_kernel, into the dQ output's
-// memory before dQ is written) for the dK/dV kernel; the dQ kernel, which runs last,
-// computes it for its own rows. All products run on
+//     dV^T = dO^T P and dK^T = Q^T dS, reading D;
+//   * fa_bwd_dq_kernel: one workgroup per 128 query rows (32 per wave) walks the key
+//     tiles, recomputing S^T and dP^T with the row on the lane (as in the forward), and
+//     accumulates dQ^T = K^T dS^T; it computes D for its own rows and then overwrites
+//     that memory with dQ.
+// All products run on
 // v_mfma_f32_32x32x16_{bf16,f16}; an accumulator becomes a 16-bit B operand of the next
 // product by the row permutation of the forward kernels (bits 2 and 3 of the MFMA row
 // swapped). Tiles are staged in LDS through registers (the next tile's loads are in
@@ -33,6 +34,14 @@
 // softmax terms (1, measured +2-4%) or one block at a time (0)
 #ifndef FA_BWD_PIPE
 #define FA_BWD_PIPE 1
+#endif
+// dQ: an interleave pattern for the machine scheduler that keeps the LDS operand reads
+// FA_BWD_DQ_AHEAD products ahead of the MFMAs that use them (1, measured +1-2%)
+#ifndef FA_BWD_DQ_SG
+#define FA_BWD_DQ_SG 1
+#endif
+#ifndef FA_BWD_DQ_AHEAD
+#define FA_BWD_DQ_AHEAD 2
 #endif
 
 namespace fa {
@@ -264,6 +273,23 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
           dq[db] = E::mfma(bwd_tr_frag<D>(ks, troff, db, 2 * kb + s2), dsop[s2], dq[db]);
+#if FA_BWD_DQ_SG
+      // operand reads run FA_BWD_DQ_AHEAD products ahead: S^T and dP^T (one row read
+      // each), then dQ (two transposed reads each); one ordered sequence over both
+      // 32-key blocks
+      __builtin_amdgcn_sched_group_barrier(0x100, FA_BWD_DQ_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * NDS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + FA_BWD_DQ_AHEAD < 2 * NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FA_BWD_DQ_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + FA_BWD_DQ_AHEAD < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#endif
     }
   }
   if (wave_live && qi < N) bwd_store_rows<BF16, D>(p.dq + head, dq, qi, hh, p.scale);
