@@ -263,3 +263,14 @@ def test_forward_rejects_bad_tensors():
         fa.forward(y, y, y)  # CPU tensors are refused before any library call
     with pytest.raises(ValueError):
         fa.forward(y, y, torch.zeros(1, 1, 8, 4, dtype=torch.bfloat16))
+
+
+def test_build_compiles_every_source():
+    # the library is linked from one object per HIP source: a source missing from the
+    # build list would leave its entry points or kernels out of libfa.so
+    from io_aware_exact_fa2_amd import build
+    csrc = os.path.join(ROOT, "io_aware_exact_fa2_amd", "csrc")
+    hip = {f for f in os.listdir(csrc) if f.endswith(".hip")}
+    assert set(build.SOURCES) == hip
+    for own in build.SOURCES.values():
+        assert all(isinstance(f, str) for f in own)
