@@ -23,10 +23,10 @@
 // All products run on
 // v_mfma_f32_32x32x16_{bf16,f16}; an accumulator becomes a 16-bit B operand of the next
 // product by the row permutation of the forward kernels (bits 2 and 3 of the MFMA row
-// swapped). Tiles are staged in LDS (dQ: through registers; dK/dV: by buffer-to-LDS
-// copies into two buffers), the next tile's loads in flight while the current one is
-// computed, with a swizzle that keeps both the row reads and the transposed reads
-// (ds_read_b64_tr_b16) free of bank conflicts.
+// swapped). Tiles are staged in LDS by buffer-to-LDS copies into two buffers, the next
+// tile's copies in flight while the current one is computed, with a swizzle that keeps
+// both the row reads and the transposed reads (ds_read_b64_tr_b16) free of bank
+// conflicts.
 #pragma once
 
 #include "fa_common.hpp"
@@ -77,35 +77,6 @@ template <int D> __device__ __forceinline__ int swz_b(int row) {
   return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
                   : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
-
-// Rows [r0, r0 + ROWS) of a [N, D] matrix held in registers on their way to LDS: all
-// threads of the workgroup load whole 16-byte chunks, so the next tile's loads can be in
-// flight while the current tile is computed.
-template <int D, int ROWS, int NT>
-struct BwdTile {
-  static constexpr int CPR = D / 8, PER = ROWS * CPR / NT;
-  static_assert((ROWS * CPR) % NT == 0, "whole chunks per thread");
-  u32x4_t x[PER];
-  // chunk t of this thread: row tid / CPR + t * NT / CPR, chunk tid % CPR
-  static __device__ __forceinline__ int row_of(int tid, int t) { return (tid + NT * t) / CPR; }
-  // Rows past N repeat row N - 1: finite data whose probabilities the kernels' masks set
-  // to zero, so every score, P and dS of such a row is 0 or masked. No select or branch
-  // touches the loaded value, so its wait stays at the store, after the current tile.
-  __device__ __forceinline__ void load(const uint16_t* src, int r0, int N, int tid) {
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int row = row_of(tid, t), ch = tid % CPR;
-      x[t] = ld16(src + (size_t)min(r0 + row, N - 1) * D + ch * 8);
-    }
-  }
-  __device__ __forceinline__ void store(u32x4_t* lds, int tid) const {
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int row = row_of(tid, t), ch = tid % CPR;
-      lds[row * CPR + (ch ^ swz_b<D>(row))] = x[t];
-    }
-  }
-};
 
 // Per-lane byte offsets of the transposed operand reads (A = M^T over 16 rows of a
 // staged tile, one 32-column block db): half h covers rows 4h .. 4h+3 of each 8-row
@@ -186,8 +157,8 @@ template <bool BF16, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
   using E = Elt<BF16>;
   constexpr int NW = 4, BQ = 128, BK = 64, CPR = D / 8, NDS = D / 16;
-  __shared__ __attribute__((aligned(1024))) u32x4_t ks[BK * CPR];
-  __shared__ __attribute__((aligned(1024))) u32x4_t vs[BK * CPR];
+  __shared__ __attribute__((aligned(1024))) u32x4_t ks2[2][BK * CPR];
+  __shared__ __attribute__((aligned(1024))) u32x4_t vs2[2][BK * CPR];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, l32 = lane & 31, hh = lane >> 5;
   const int N = p.N;
   const int n_qt = (N + BQ - 1) / BQ;
@@ -230,20 +201,46 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) troff[db][h] = bwd_tr_off<D>(lane, db, h);
 
-  BwdTile<D, BK, NW * 64> kt_next, vt_next;
-  kt_next.load(p.k + head, 0, N, tid);
-  vt_next.load(p.v + head, 0, N, tid);
+  // Key tiles: K and V go HBM -> LDS by buffer loads with an LDS destination into two
+  // buffers (tile j in buffer j % 2; iteration j issues tile j+1 into the other one,
+  // whose readers passed the previous barrier), one barrier per tile. Lane l of copy c
+  // writes chunk (wid + NW c) * 64 + l and fetches the logical chunk the swizzle puts
+  // there; the buffer range ends at key N, so keys past N read as zeros (masked).
+  constexpr int TOT = BK * CPR, PERW = TOT / (64 * NW);
+  static_assert(TOT % (64 * NW) == 0, "whole 1 KB copies per wave");
+  const int wu = __builtin_amdgcn_readfirstlane(wid);  // LDS destination base: wave-uniform
+  int doff[PERW];
+#pragma unroll
+  for (int c = 0; c < PERW; ++c) {
+    const int f = (wid + NW * c) * 64 + lane, row = f / CPR, ph = f % CPR;
+    doff[c] = row * D + (ph ^ swz_b<D>(row)) * 8;
+  }
+  auto issue = [&](int kb0, u32x4_t* kdst, u32x4_t* vdst) {
+    const int bytes = min(N - kb0, BK) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.k + head + (size_t)kb0 * D), (short)0, bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.v + head + (size_t)kb0 * D), (short)0, bytes, kBufferWord3);
+    // (the LDS destinations and offsets are arguments: a lambda that captured the shared
+    // arrays or the offset array here made the host pass drop the kernel's launch stub)
+    auto copy = [&](int c, int off) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + (wu + NW * c) * 64), 16,
+                                               off * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + (wu + NW * c) * 64), 16,
+                                               off * 2, 0, 0, 0);
+    };
+#pragma unroll
+    for (int c = 0; c < PERW; ++c) copy(c, doff[c]);
+  };
+  issue(0, ks2[0], vs2[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   for (int j = 0; j < n_kt; ++j) {
-    const int k0 = j * BK;
-    __syncthreads();  // the previous tile's reads are done
-    kt_next.store(ks, tid);
-    vt_next.store(vs, tid);
-    __syncthreads();
-    if (j + 1 < n_kt) {  // in flight while this tile is computed
-      kt_next.load(p.k + head, k0 + BK, N, tid);
-      vt_next.load(p.v + head, k0 + BK, N, tid);
-    }
-    if (!wave_live || (CAUSAL && k0 > w_last)) continue;
+    const int k0 = j * BK, b = j & 1;
+    if (j + 1 < n_kt) issue(k0 + BK, ks2[b ^ 1], vs2[b ^ 1]);
+    const u32x4_t* ks = ks2[b];
+    const u32x4_t* vs = vs2[b];
+    if (wave_live && !(CAUSAL && k0 > w_last)) {  // every wave copies and meets the barrier
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb) {
       // S^T and dP^T of 32 keys x this wave's 32 queries
@@ -292,6 +289,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
       }
 #endif
     }
+    }  // live tile
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile j+1's copies
+    __syncthreads();
   }
   if (wave_live && qi < N) bwd_store_rows<BF16, D>(p.dq + head, dq, qi, hh, p.scale);
 }
