@@ -110,6 +110,13 @@ def test_backward_sequence_lengths(N, causal):
     _case(Workload(f"N{N}", 1, 2, N, 128, "bf16", causal, seed=7500 + N))
 
 
+@pytest.mark.parametrize("N", [1, 65, 127, 128, 129, 255, 257, 383])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sequence_lengths_d64(N, causal):
+    # d = 64 stages 128-query tiles in the dK/dV kernel: lengths around its tile edges
+    _case(Workload(f"N{N}d64", 1, 2, N, 64, "fp16", causal, seed=7700 + N))
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 0.02, 0.5])
 def test_backward_scale_values(scale):
     for causal in (False, True):
