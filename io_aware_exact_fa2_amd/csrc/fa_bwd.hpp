@@ -300,10 +300,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
 template <bool BF16, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  // Queries per staged tile: 128 halves the copies, barriers and loop overhead per
-  // query (causal and d = 64: +2 to +7%); non-causal d = 128 keeps 64, where the longer
-  // unrolled tile spills registers (-1%).
-  constexpr int BQ = (D == 128 && !CAUSAL) ? 64 : 128;
+  // Queries per staged tile: 128 rather than 64 halves the copies, barriers and loop
+  // overhead per query (+2 to +7%).
+  constexpr int BQ = 128;
   constexpr int NW = 4, BKV = 128, CPR = D / 8, NDS = D / 16;
   __shared__ __attribute__((aligned(1024))) u32x4_t qs2[2][BQ * CPR];
   __shared__ __attribute__((aligned(1024))) u32x4_t dos2[2][BQ * CPR];
@@ -469,8 +468,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
     };
     static_assert(BQ % 64 == 0, "pairs of 32-query blocks per tile");
     if constexpr (D == 128 && FA_BWD_PIPE) {  // both blocks' S and dP of a pair first
-#pragma unroll
-      for (int q2 = 0; q2 < BQ / 32; q2 += 2) {
+      auto pair = [&](int q2) {
         f32x16_t s0, dp0, s1, dp1;
         u32x4_t pop0[2], dsop0[2], pop1[2], dsop1[2];
         sdp(q2, s0, dp0);
@@ -479,6 +477,15 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
         accum(q2, pop0, dsop0);
         soft(q2 + 1, s1, dp1, pop1, dsop1);
         accum(q2 + 1, pop1, dsop1);
+      };
+      // unrolled, the non-causal tile spills registers (-1%); rolled it is 3-4% faster,
+      // while the causal tile is 1% faster unrolled
+      if constexpr (CAUSAL) {
+#pragma unroll
+        for (int q2 = 0; q2 < BQ / 32; q2 += 2) pair(q2);
+      } else {
+#pragma unroll 1
+        for (int q2 = 0; q2 < BQ / 32; q2 += 2) pair(q2);
       }
     } else {  // d = 64 keeps two waves per SIMD with one block at a time
 #pragma unroll
