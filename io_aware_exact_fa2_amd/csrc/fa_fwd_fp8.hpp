@@ -19,10 +19,10 @@
 // in block kb hold keys 32 h + 16 kb + r (r = 0..15): packed to bytes, the two blocks are
 // exactly the 32 consecutive keys that lane half h supplies as the B operand of the
 // 64-key P V product. V^T operands are read with ds_read_b64_tr_b8 (each lane of a
-// 16-lane group receives one column of 8 rows). Tiles are staged through registers, the
-// next tile's loads in flight while the current one is computed, into two LDS buffers
-// (one barrier per tile). Workgroups of NW waves of 32 queries each (4 by default: three
-// workgroups share a CU).
+// 16-lane group receives one column of 8 rows). Tiles go HBM -> LDS by buffer-to-LDS
+// copies into two buffers, the next tile's copies in flight while the current one is
+// computed (one barrier per tile). Workgroups of NW waves of 32 queries each (4 by
+// default: three workgroups share a CU at d = 128).
 #pragma once
 
 #include "fa_common.hpp"
@@ -70,7 +70,6 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   constexpr int BR = NW * 32, BC = 64, CPR = D / 16;  // 16-byte chunks per row
   constexpr int NT = D / 64;                                  // 64-deep MFMA steps over d
   constexpr int TOT = BC * CPR;                               // chunks per tile and tensor
-  constexpr int PER = (TOT + NW * 64 - 1) / (NW * 64);        // chunks per thread per tile
   static_assert(D == 64 || D == 128, "head dims");
   __shared__ __attribute__((aligned(1024))) u32x4_t ks2[2][BC * CPR];
   __shared__ __attribute__((aligned(1024))) u32x4_t vs2[2][BC * CPR];
@@ -135,30 +134,38 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
     return r;
   };
 
-  // staging: thread chunk t -> row (tid + 64 NW t) / CPR, chunk tid % CPR (threads past
-  // the tile's chunks idle)
-  u32x4_t kn[PER], vn[PER];
-  // Rows past N repeat row N - 1 (finite; their scores are masked to -inf, so their
-  // probabilities are 0); no select touches the loaded values before the store.
-  auto fetch = [&](int j) {
+  // Tiles go HBM -> LDS by buffer loads with an LDS destination (no register staging).
+  // Each wave copies whole 1 KB pieces: lane l of copy c writes chunk (wid + NW c) * 64 + l
+  // of the tile and fetches the logical chunk that the tensor's swizzle puts there. The
+  // buffer range ends at key N, so rows past N read as zero bytes (+0 in E4M3; their
+  // scores are masked to -inf, so their probabilities are 0).
+  constexpr int PERW = TOT / (64 * NW);
+  static_assert(TOT % (64 * NW) == 0, "whole 1 KB copies per wave");
+  int koff[PERW], voff[PERW];
+#pragma unroll
+  for (int cc = 0; cc < PERW; ++cc) {
+    const int f = (wid + NW * cc) * 64 + lane, row = f / CPR, ph = f % CPR;
+    koff[cc] = row * D + (ph ^ swz8_k<D>(row)) * 16;
+    voff[cc] = row * D + (ph ^ swz8_v<D>(row)) * 16;
+  }
+  auto issue = [&](int j, u32x4_t* kdst, u32x4_t* vdst) {
     const int k0 = j * BC;
+    const int bytes = min(N - k0, BC) * D;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(kg + (size_t)k0 * D), (short)0, bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(vg + (size_t)k0 * D), (short)0, bytes, kBufferWord3);
+    // (destinations and offsets are arguments: a lambda that captured the shared arrays
+    // or the offset arrays here made the host pass drop the kernel's launch stub; wid is
+    // wave-uniform, read from the first lane, as the LDS destination base must be)
+    auto copy = [&](int cc, int ko, int vo) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + (wid + NW * cc) * 64), 16,
+                                               ko, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + (wid + NW * cc) * 64), 16,
+                                               vo, 0, 0, 0);
+    };
 #pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int idx = min(tid + NW * 64 * t, TOT - 1), row = idx / CPR, ch = idx % CPR;
-      const size_t off = (size_t)min(k0 + row, N - 1) * D + ch * 16;
-      kn[t] = *reinterpret_cast<const u32x4_t*>(kg + off);
-      vn[t] = *reinterpret_cast<const u32x4_t*>(vg + off);
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < PER; ++t) {
-      const int idx = tid + NW * 64 * t, row = idx / CPR, ch = idx % CPR;
-      if (idx < TOT) {
-        ks2[buf][row * CPR + (ch ^ swz8_k<D>(row))] = kn[t];
-        vs2[buf][row * CPR + (ch ^ swz8_v<D>(row))] = vn[t];
-      }
-    }
+    for (int cc = 0; cc < PERW; ++cc) copy(cc, koff[cc], voff[cc]);
   };
 
   f32x16_t oacc[D / 32];
@@ -169,15 +176,15 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
   float ms = -__builtin_inff(), l_part = 0.f;
   const float c = p.c;
 
-  // Tile t lives in buffer t % 2. Iteration j computes tile j, stores tile j+1 (already
-  // in registers) into the other buffer, whose last readers (tile j-1) all passed the
-  // previous barrier, then waits at one barrier and issues the loads of tile j+2.
-  fetch(0);
-  stage(0);
+  // Tile t lives in buffer t % 2. Iteration j issues the copies of tile j+1 into the
+  // other buffer, whose last readers (tile j-1) all passed the previous barrier, computes
+  // tile j, waits for its own copies and meets one barrier.
+  issue(0, ks2[0], vs2[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (n_kt > 1) fetch(1);
   for (int j = 0; j < n_kt; ++j) {
     const int k0 = j * BC;
+    if (j + 1 < n_kt) issue(j + 1, ks2[(j + 1) & 1], vs2[(j + 1) & 1]);
     const u32x4_t* ks = ks2[j & 1];
     const u32x4_t* vs = vs2[j & 1];
     if (wave_live && j < w_kt) {
@@ -242,9 +249,8 @@ fa_fwd_fp8_kernel(const Fp8Params p) {
         oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_op(vs, db), pb, oacc[db], 0, 0, 0,
                                                                    0, 0, 0);
     }
-    if (j + 1 < n_kt) stage((j + 1) & 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // tile j+1's copies
     __syncthreads();
-    if (j + 2 < n_kt) fetch(j + 2);
   }
 
   // epilogue: O = vs * O~ / l (bfloat16; the 2^6 cancels), L = (m - 6 + log2 l) ln 2
