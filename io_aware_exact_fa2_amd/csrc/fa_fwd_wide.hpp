@@ -662,27 +662,76 @@ fa_fwd_wide_kernel(const Params p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
-  if (!wave_live) return;
-  const float kLn2 = 0.69314718055994530942f;
+  // Under the causal mask the waves of a workgroup finish at different times: each
+  // stores its rows directly (8-byte pieces) as soon as it is done. Without the mask they
+  // finish together, and the rows go out through LDS as whole-row chunks (ai2048 +3%;
+  // the barrier this needs cost 1.5% on long causal runs).
+  if constexpr (CAUSAL) {
+    if (!wave_live) return;
+    const float kLn2 = 0.69314718055994530942f;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    drain_o(qb);
-    const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
-    const int qi = qbase[qb] + l32;
-    if (qi < N) {
+    for (int qb = 0; qb < 2; ++qb) {
+      drain_o(qb);
+      const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
+      const int qi = qbase[qb] + l32;
+      if (qi < N) {
+        const float inv = 1.0f / l_tot;
+        uint16_t* orow = p.o + head + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dcol = db * 32 + g * 8 + hh * 4;
+            const f32x16_t& a = oacc[db][qb];
+            const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
+            const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+            *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
+          }
+        if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      }
+    }
+  } else {
+    // O leaves through LDS: each wave writes its 64 rows (the accumulator layout gives a
+    // lane 8 bytes of one row per write) into its own part of the K ring, then stores them
+    // as 16-byte chunks of whole rows (a store instruction covers 64 / CPR whole rows),
+    // instead of scattering 8-byte pieces over 32 rows per instruction. Chunk c of row r
+    // sits at chunk c ^ (r % CPR) of the row, so neither side conflicts on banks. The
+    // barrier makes every wave's last copies land before the ring is reused.
+    static_assert(R * CHUNKS >= NW * 64 * CPR && (CPR & (CPR - 1)) == 0 && CPR <= 64,
+                  "a 64-row O tile per wave fits the K ring");
+    ring_barrier();
+    if (!wave_live) return;
+    const float kLn2 = 0.69314718055994530942f;
+    unsigned char* ot = reinterpret_cast<unsigned char*>(kbuf + wid * 64 * CPR);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      drain_o(qb);
+      const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
       const float inv = 1.0f / l_tot;
-      uint16_t* orow = p.o + head + (size_t)qi * D;
+      const int rr = 32 * qb + l32;  // row of the wave's tile
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int dcol = db * 32 + g * 8 + hh * 4;
           const f32x16_t& a = oacc[db][qb];
           const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
           const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-          *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
+          const int c = db * 4 + g;  // 16-byte chunk of the row; this lane holds half hh
+          *reinterpret_cast<u32x2_t*>(ot + (rr * CPR + (c ^ (rr & (CPR - 1)))) * 16 + hh * 8) =
+              u32x2_t{w0, w1};
         }
-      if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      const int qi = qbase[qb] + l32;
+      if (qi < N && hh == 0)
+        p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+#pragma unroll
+    for (int it = 0; it < CPR; ++it) {
+      const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
+      const u32x4_t x =
+          *reinterpret_cast<const u32x4_t*>(ot + (rr * CPR + (c ^ (rr & (CPR - 1)))) * 16);
+      const int qi = qbase[rr >> 5] + (rr & 31);
+      if (qi < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)qi * D + c * 8) = x;
     }
   }
 }
