@@ -424,10 +424,10 @@ fa_fwd_fast_kernel(const Params p) {
   if (!wave_live) return;
   const float kLn2 = 0.69314718055994530942f;
   const float l_tot = xhalf_sum(l_part);
-  const int qi = wq0 + l32;
-  if (qi >= N) return;
+  const int qi = wq0 + l32;  // rows past N (finite, from clamped or zero rows) are never stored
   const float inv = 1.0f / l_tot;
   if constexpr (SPLIT) {
+    if (qi >= N) return;
     const size_t row = ((size_t)split * p.BH + bh) * N + qi;
     float* prow = p.o_part + row * D;
 #pragma unroll
@@ -441,18 +441,33 @@ fa_fwd_fast_kernel(const Params p) {
     if (hh == 0) p.l_part[row] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
     return;
   }
-  uint16_t* orow = p.o + head + (size_t)qi * D;
+  // O leaves through LDS (the loop ended at a barrier after every copy landed, so the K
+  // and V slots are idle): the wave writes its 32 rows into its own part of them (a lane
+  // holds 8 bytes of one row per write) and stores 16-byte chunks of whole rows, instead
+  // of 8-byte pieces over 32 rows per store instruction. Chunk c of row r sits at chunk
+  // c ^ (r % CPR) of the row (no bank conflicts on either side).
+  static_assert(NW <= 4 && 2 * 32 * CPR <= G::CHUNKS, "two waves' O tiles fit one slot");
+  unsigned char* ot = reinterpret_cast<unsigned char*>((wid < 2 ? ks0 : vs0) + (wid & 1) * 32 * CPR);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int dcol = db * 32 + g * 8 + hh * 4;
       const f32x16_t& a = oacc[db];
       const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
       const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-      *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
+      const int c = db * 4 + g;  // 16-byte chunk of row l32; this lane holds half hh
+      *reinterpret_cast<u32x2_t*>(ot + (l32 * CPR + (c ^ (l32 & (CPR - 1)))) * 16 + hh * 8) =
+          u32x2_t{w0, w1};
     }
-  if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  if (hh == 0 && qi < N) p.lse[(size_t)bh * N + qi] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+#pragma unroll
+  for (int it = 0; it < CPR / 2; ++it) {
+    const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
+    const u32x4_t x =
+        *reinterpret_cast<const u32x4_t*>(ot + (rr * CPR + (c ^ (rr & (CPR - 1)))) * 16);
+    if (wq0 + rr < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)(wq0 + rr) * D + c * 8) = x;
+  }
 }
 
 }  // namespace fa
