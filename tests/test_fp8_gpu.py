@@ -172,6 +172,34 @@ def test_fp8_full_ai2048_sampled():
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
 
 
+def test_fp8_full_ai2048_every_row():
+    """The full B=4, H=16, N=2048, d=128 shape in one launch: every row of every head
+    against the oracle on the decoded inputs, under the bar above (the per-head bound
+    terms are computed on the host cores in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    w = workloads.get("ai2048")
+    q8, k8, v8, qs, ks, vs = workloads.make_fp8_inputs(w)
+    o, lse = fa.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), qs, ks, vs, scale=w.scale)
+    torch.cuda.synchronize()
+    O, L = oracle.attention_fp8(q8.numpy(), k8.numpy(), v8.numpy(), qs, ks, vs, w.scale, False)
+    q, k, v = (oracle.decode_e4m3(t.numpy()) * s for t, s in ((q8, qs), (k8, ks), (v8, vs)))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(bh):
+        b, h = bh
+        return _bounds(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                       w.scale, False, L[b:b + 1, h:h + 1])
+
+    from oracle.attention import default_workers
+
+    with ThreadPoolExecutor(max_workers=default_workers()) as ex:
+        parts = list(ex.map(one, heads))
+    bounds = tuple(np.stack([pt[j][0, 0] for pt in parts]).reshape(
+        (w.B, w.H) + parts[0][j].shape[2:]) for j in range(3))
+    _check("fp8/ai2048/every_row", o, lse, O, L, bounds)
+
+
 def test_fp8_raw_abi_errors():
     w = Workload("raw", 1, 2, 100, 64, "bf16", False, seed=9500)
     q8, k8, v8, qs, ks, vs = (x.to(DEV) if torch.is_tensor(x) else x

@@ -2,9 +2,9 @@
 
 Bars (max-abs over every compared element): O within 1.5e-2 for bfloat16 and
 5e-3 for float16, L within 1e-3. Reduced shapes that span several tiles and a
-ragged tail are compared element by element; the five full-size workloads are
-compared on sampled rows (first, last, tile-boundary and random rows of several
-heads) and checked on every row with properties that hold at any size.
+ragged tail are compared element by element, and so is every row of every head of the four
+full-size workloads (one launch each, as the benchmark times them); a sampled-row
+variant and properties that hold at any size run beside them.
 """
 import json
 import math
@@ -252,6 +252,23 @@ def test_full_workload_sampled(name):
     assert bool((lse >= s0 - TOL_L).all())
     del qd, kd, vd, of, lo, hi
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_every_row(name):
+    """Every row of every head of the full-size workload, element by element against the
+    float64 oracle, in the launch configuration the benchmark times (one launch over the
+    whole batch, so the full grid's tile order and the next-round cache warming run)."""
+    w = workloads.get(name)
+    _full_case(w, name=f"{name}/every_row")
+
+
+def test_full_stress_every_row_literal_update():
+    """The per-block max update as the pages write it (threshold 0: the reference max is
+    raised on every key block that exceeds it), on every row of the full spiked-key
+    workload, against the oracle."""
+    w = workloads.get("stress4000")
+    _full_case(w, rescale_log2=0.0, name="stress4000/every_row/tau=0")
 
 
 @pytest.mark.parametrize("name", ["causal8k", "long32k"])
