@@ -13,13 +13,14 @@
  *
  * The library never allocates device memory, keeps no pointer after a call returns
  * and needs no workspace except where an entry point takes one from the caller (the O(N)
- * extra memory of the [P1] "정리" comparison table is the L output itself). Its only
- * global state is the compute-unit count and the LDS size per compute unit of each
+ * extra memory of the [P1] "정리" comparison table is the L output itself); the one
+ * exception, fa_fwd_splitkv_static, uses a fixed device array of its own. Its only
+ * other global state is the compute-unit count and the LDS size per compute unit of each
  * device, read once per device (std::call_once) and immutable afterwards; they only
  * steer which of the call's own Q and K rows a workgroup pre-loads into the L2 and how
  * many 8-bit workgroups share a compute unit (performance hints, never correctness
- * inputs). Calls are reentrant and
- * thread-safe. No C++ exception crosses this boundary.
+ * inputs). Calls are reentrant and thread-safe (fa_fwd_splitkv_static: see its
+ * comment). No C++ exception crosses this boundary.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -38,7 +39,8 @@ enum fa_status {
   FA_ERR_UNSUPPORTED = -3, /* d > 128, or an unknown dtype code                           */
   FA_ERR_ALIAS = -4,       /* o or lse overlaps q, k, v, or each other                    */
   FA_ERR_ALIGN = -5,       /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned   */
-  FA_ERR_HIP = -6          /* the HIP runtime refused the launch; see fa_last_hip_error() */
+  FA_ERR_HIP = -6,         /* the HIP runtime refused the launch; see fa_last_hip_error() */
+  FA_ERR_SCRATCH = -7      /* fa_fwd_splitkv_static: partials exceed the static scratch   */
 };
 
 /* dtype codes for fa_fwd_ex() and fa_fwd_supported(). */
@@ -51,6 +53,9 @@ enum fa_dtype { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 };
 
 /* Largest split count fa_fwd_splitkv accepts. */
 #define FA_MAX_SPLITS 64
+
+/* Bytes of the device-resident scratch array behind fa_fwd_splitkv_static (64 MiB). */
+#define FA_STATIC_SCRATCH_BYTES (64u << 20)
 
 /*
  * fa_fwd — exact attention forward in the FA2 loop order, bfloat16 tensors.
@@ -193,6 +198,31 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 /* Bytes of workspace fa_fwd_splitkv needs for these sizes; 0 when they are invalid
  * (B, H, N < 1, d not 64 or 128, n_splits outside [1, FA_MAX_SPLITS]). Host only. */
 size_t fa_fwd_splitkv_workspace_size(int B, int H, int N, int d, int n_splits);
+
+/*
+ * fa_fwd_splitkv_static — fa_fwd_splitkv without the workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid allocation. It allocates nothing: the float32 partials live
+ * in a file-scope device array of FA_STATIC_SCRATCH_BYTES bytes that each GPU the
+ * library runs on holds from the library's first use on that GPU until the process
+ * ends. The array's device address is looked up once per device (hipGetSymbolAddress,
+ * with that device current) on the first call on the device; that lookup failing
+ * returns FA_ERR_HIP.
+ *
+ * Same operation, arguments, validation and asynchrony as fa_fwd_splitkv with the
+ * caller's workspace replaced by that array. A call whose partials
+ * (fa_fwd_splitkv_workspace_size(B, H, N, d, n_splits) bytes) exceed
+ * FA_STATIC_SCRATCH_BYTES returns FA_ERR_SCRATCH before any HIP call. The partial pass
+ * writes every partial the merge reads, so nothing needs clearing between calls.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its partials there: calls
+ * that overlap in time on one GPU (on different streams, or from several threads without
+ * ordering) race on it and give unspecified results. Calls ordered on one stream are
+ * safe.
+ */
+int fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal, int n_splits,
+                          int dtype, void* stream);
 
 /*
  * fa_fwd_fa1 — the same outputs as fa_fwd_ex (up to rounding), computed in the FA1

@@ -23,7 +23,8 @@ __all__ = [
     "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
     "fa_bwd", "fa_bwd_fp16", "backward", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
     "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "forward_splitkv", "forward_fa1", "FA_MAX_SPLITS",
-    "fa_fwd_fp8", "forward_fp8", "fa_device_supported",
+    "fa_fwd_fp8", "forward_fp8", "fa_device_supported", "fa_fwd_splitkv_static",
+    "FA_ERR_SCRATCH", "FA_STATIC_SCRATCH_BYTES",
     "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
 ]
@@ -35,14 +36,17 @@ FA_ERR_UNSUPPORTED = -3
 FA_ERR_ALIAS = -4
 FA_ERR_ALIGN = -5
 FA_ERR_HIP = -6
+FA_ERR_SCRATCH = -7
 FA_DTYPE_BF16 = 0
 FA_DTYPE_FP16 = 1
 
 EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_fwd_splitkv_static",
            "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
            "fa_device_supported",
            "fa_strerror", "fa_last_hip_error", "fa_version")
 FA_MAX_SPLITS = 64
+FA_STATIC_SCRATCH_BYTES = 64 << 20
 FA_DEFAULT_RESCALE_LOG2 = 8.0
 FA_MAX_RESCALE_LOG2 = 15.0
 
@@ -86,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_fp8.restype = i
     L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, i, vp]
     L.fa_fwd_splitkv.restype = i
+    L.fa_fwd_splitkv_static.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]
+    L.fa_fwd_splitkv_static.restype = i
     L.fa_fwd_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     L.fa_fwd_splitkv_workspace_size.restype = sz
     L.fa_fwd_fa1.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
@@ -158,6 +164,15 @@ def fa_fwd_splitkv(q, k, v, o, lse, workspace, workspace_bytes, B, H, N, d, scal
     return lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                 int(workspace_bytes), B, H, N, d, float(scale), int(causal),
                                 int(n_splits), int(dtype), _stream(stream))
+
+
+def fa_fwd_splitkv_static(q, k, v, o, lse, B, H, N, d, scale, causal, n_splits, dtype,
+                          stream=None) -> int:
+    """C ``fa_fwd_splitkv_static``: ``fa_fwd_splitkv`` on the library's own device scratch
+    (no workspace argument; nothing allocated)."""
+    return lib().fa_fwd_splitkv_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                                       d, float(scale), int(causal), int(n_splits), int(dtype),
+                                       _stream(stream))
 
 
 def fa_fwd_splitkv_workspace_size(B, H, N, d, n_splits) -> int:

@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -282,6 +283,45 @@ int fa_splitkv_impl(const void* q, const void* k, const void* v, void* o, float*
   return FA_OK;
 }
 
+// ---- split-KV on the library's own scratch (for callers that cannot allocate) ---------
+// The partials of fa_fwd_splitkv_static live in this file-scope device array; each GPU
+// holds its own copy from the code object's load until the process ends. In host code
+// `scratch` only names a host-side stand-in: kernels get the device address looked up
+// below, never the name.
+static __device__ __align__(256) unsigned char scratch[FA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// Device address of the current device's `scratch`, looked up once per device with that
+// device current (the first call on it) and kept for later calls.
+int static_scratch(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  ScratchAddr& a = g_scratch[dev];
+  std::call_once(a.once, [&a]() {
+    void* ptr = nullptr;
+    a.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    a.ptr = a.err == hipSuccess ? ptr : nullptr;
+  });
+  if (a.err != hipSuccess || a.ptr == nullptr) {
+    g_last_hip_error = static_cast<int>(a.err != hipSuccess ? a.err : hipErrorInvalidSymbol);
+    return FA_ERR_HIP;
+  }
+  *out = a.ptr;
+  return FA_OK;
+}
+
 template <bool BF16>
 int fa_fa1_impl(const void* q, const void* k, const void* v, void* o, float* lse, void* ws,
                 size_t ws_bytes, int B, int H, int N, int d, float scale, int causal, void* stream) {
@@ -436,6 +476,28 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return FA_ERR_UNSUPPORTED;
 }
 
+int fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int causal, int n_splits,
+                          int dtype, void* stream) {
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP16) return FA_ERR_UNSUPPORTED;
+  // the checks of fa_fwd_splitkv that do not involve the workspace, before any HIP call
+  int st = validate(q, k, v, o, lse, B, H, N, d, scale, 0.f);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (scale == 0.f) return FA_ERR_SHAPE;
+  const size_t need = splitkv_bytes(B, H, N, d, n_splits);
+  if (need == 0) return FA_ERR_SHAPE;
+  if (need > FA_STATIC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != FA_OK) return st;
+  if (dtype == FA_DTYPE_BF16)
+    return fa_splitkv_impl<true>(q, k, v, o, lse, ws, FA_STATIC_SCRATCH_BYTES, B, H, N, d,
+                                 scale, causal, n_splits, stream);
+  return fa_splitkv_impl<false>(q, k, v, o, lse, ws, FA_STATIC_SCRATCH_BYTES, B, H, N, d,
+                                scale, causal, n_splits, stream);
+}
+
 size_t fa_fwd_fa1_workspace_size(int B, int H, int N, int d) { return fa1_bytes(B, H, N, d); }
 
 int fa_fwd_fa1(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -503,6 +565,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "o or lse overlaps q, k, v or each other";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_HIP: return "the HIP runtime refused the launch (see fa_last_hip_error)";
+    case FA_ERR_SCRATCH: return "split-KV partials exceed the library's static scratch (FA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_strerror_and_version(L):
     for code in (fa.FA_OK, fa.FA_ERR_NULL, fa.FA_ERR_SHAPE, fa.FA_ERR_UNSUPPORTED,
-                 fa.FA_ERR_ALIAS, fa.FA_ERR_ALIGN, fa.FA_ERR_HIP):
+                 fa.FA_ERR_ALIAS, fa.FA_ERR_ALIGN, fa.FA_ERR_HIP, fa.FA_ERR_SCRATCH):
         assert fa.fa_strerror(code) and fa.fa_strerror(code) != "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
     assert "gfx950" in fa.fa_version()
@@ -219,6 +219,33 @@ def test_workspace_pass_validation(L, no_gpu, which):
             <= 3 * per_split(300) + 512
         assert 8 * per_split(1000) <= fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) \
             <= 8 * per_split(1000) + 512
+    assert fa.fa_last_hip_error() == 0
+
+
+def test_static_scratch_splitkv_validation(L, no_gpu):
+    """fa_fwd_splitkv_static refuses, before any HIP call, everything fa_fwd_splitkv
+    refuses apart from the workspace checks, and partials larger than its static scratch
+    (FA_ERR_SCRATCH)."""
+    G = dict(GOOD, d=64)
+
+    def call(ns=4, dtype=fa.FA_DTYPE_BF16, o=OA, lse=LA, **kw):
+        a = dict(G, **kw)
+        return fa.fa_fwd_splitkv_static(QA, KA, VA, o, lse, a["B"], a["H"], a["N"], a["d"],
+                                        a["scale"], a["causal"], ns, dtype, None)
+
+    assert call(o=0) == fa.FA_ERR_NULL
+    assert call(o=QA) == fa.FA_ERR_ALIAS
+    assert call(N=0) == fa.FA_ERR_SHAPE
+    assert call(scale=0.0) == fa.FA_ERR_SHAPE
+    assert call(ns=0) == fa.FA_ERR_SHAPE
+    assert call(ns=fa.FA_MAX_SPLITS + 1) == fa.FA_ERR_SHAPE
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(dtype=2) == fa.FA_ERR_UNSUPPORTED
+    # 4 splits of B*H*N = 2^20 rows at d = 128 need 2 GiB of partials
+    big = dict(B=1, H=64, N=16384, d=128)
+    assert fa.fa_fwd_splitkv_workspace_size(*big.values(), 4) > fa.FA_STATIC_SCRATCH_BYTES
+    assert call(**big) == fa.FA_ERR_SCRATCH
+    assert fa.fa_strerror(fa.FA_ERR_SCRATCH) != "unknown status"
     assert fa.fa_last_hip_error() == 0
 
 
