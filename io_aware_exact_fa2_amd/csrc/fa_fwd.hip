@@ -39,13 +39,6 @@ using fa_host::ranges_overlap;
 #ifndef FA_WPE_D64
 #define FA_WPE_D64 2
 #endif
-// The 64-query-per-wave kernel (one wave per SIMD) instead of the 32-query one
-#ifndef FA_WIDE_D128
-#define FA_WIDE_D128 1
-#endif
-#ifndef FA_WIDE_D64
-#define FA_WIDE_D64 0
-#endif
 #ifndef FA_WIDE_RING
 #define FA_WIDE_RING 4    // LDS ring slots per tensor
 #endif
@@ -158,11 +151,11 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
     if (d <= 64) e = cz ? launch_generic<BF16, 64, true>(p, s) : launch_generic<BF16, 64, false>(p, s);
     else e = cz ? launch_generic<BF16, 128, true>(p, s) : launch_generic<BF16, 128, false>(p, s);
   } else if (d == 128) {
-    if (FA_WIDE_D128) e = cz ? launch_wide<BF16, 128, true>(p, s) : launch_wide<BF16, 128, false>(p, s);
-    else e = cz ? launch_fast<BF16, 128, true>(p, s) : launch_fast<BF16, 128, false>(p, s);
+    // 64 queries per wave, one wave per SIMD
+    e = cz ? launch_wide<BF16, 128, true>(p, s) : launch_wide<BF16, 128, false>(p, s);
   } else {
-    if (FA_WIDE_D64) e = cz ? launch_wide<BF16, 64, true>(p, s) : launch_wide<BF16, 64, false>(p, s);
-    else e = cz ? launch_fast<BF16, 64, true>(p, s) : launch_fast<BF16, 64, false>(p, s);
+    // 32 queries per wave, two waves per SIMD
+    e = cz ? launch_fast<BF16, 64, true>(p, s) : launch_fast<BF16, 64, false>(p, s);
   }
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);

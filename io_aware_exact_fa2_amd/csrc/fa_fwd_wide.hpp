@@ -1,57 +1,48 @@
 // fa_fwd_wide.hpp — FA2-order attention forward for gfx950 (MI355X): one wave per
-// SIMD, 64 queries per wave, for head dims 64 and 128.
+// SIMD, 64 queries per wave, head dims 64 and 128, with the key tiles in a three-stage
+// pipeline and the rescale decided from row sums.
 //
 // Algorithm ([P1] currybab.bearblog.dev, "Triton으로 FlashAttention 구현하기 전에 -
 // FA1, 2 forward pass", section "FlashAttention 2 forward pass 알고리즘 분석"): the
 // query row block is the outer loop (one workgroup per query block, head and batch),
 // key/value blocks stream through LDS in the inner loop, each row keeps its running
 // max and sum on chip, rescales the unnormalised output by alpha = exp(m_old - m_new)
-// only, and divides once at the end. Waves own disjoint query rows (split-Q), so no
-// cross-wave merge exists.
+// only, and divides once at the end. Waves own disjoint query rows (split-Q).
 //
-// Why a second fast kernel: with 32 queries per wave, every K or V operand read from
-// LDS feeds exactly one 32x32x16 MFMA, and the LDS read bandwidth of a CU then equals
-// its MFMA rate, so LDS and the matrix cores bound each other. Here each wave owns
-// two 32-query column blocks and every operand read from LDS feeds two MFMAs, which
-// halves the LDS traffic per flop. The price is registers: the two output
-// accumulators alone take 128 of them at d = 128, so a wave gets the whole register
-// file of its SIMD (one wave per SIMD, four per workgroup) and hides latency by
-// software pipelining only.
+// Why this kernel. With one wave per SIMD the wave issues everything itself, and the
+// softmax's VALU work per tile (one FMA, one exponential, one add per score, half a
+// pack) is almost as long as the tile's 64 MFMAs, so the wave is issue bound. The
+// running max of each key tile (half a max3 per score, plus the cross-half exchange
+// and the vote) is the one piece of that work the method does not need on every tile:
+// the reference max only has to keep the probabilities bounded. Here a tile's softmax
+// is computed against the current reference and its probabilities are summed per lane
+// anyway; if every lane's tile sum is at most 2^tau, every probability is, and nothing
+// else happens. Only when some lane's sum exceeds 2^tau (a probability may) does the
+// wave take the row max of that tile, raise the references by the rule of the pages
+// (alpha = exp(m_old - m_new) applied to l and O~, when the max exceeds the reference
+// by more than tau) and recompute the tile's softmax. The softmax does not depend on
+// the reference (the max shift cancels, [P1] "Online Softmax 개념"), so O and L are
+// those of the per-block update up to rounding.
 //
-// gfx950 mapping:
-//   * K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register
-//     staging) into a ring of R slots each. Iteration j issues K_{j+R} and V_{j+R-1};
-//     every copy has R - 1 iterations to land, and the end-of-iteration wait leaves
-//     the newest R - 2 iterations of copies in flight (vmcnt counts this wave's copies
-//     in issue order). One barrier per iteration makes the other waves' copies
-//     visible and frees the slots for the next copies.
-//   * K runs one tile ahead of V: while tile j is finished, the S^T MFMAs of tile j+1
-//     are interleaved with the first half of the exponentials of tile j, and the P V
-//     MFMAs of tile j with the second half and then with the row max of tile j+1.
-//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}; each lane owns
-//     one query column per block, so the running max/sum and the alpha rescale are
-//     in-lane, and the S^T accumulator rounded to 16 bits is the B operand of P V
-//     (key rows enter with bits 2 and 3 of the row index swapped).
-//   * LDS layout, XOR swizzles, transposed V reads (ds_read_b64_tr_b16), exp2 with the
-//     log2(e) factor folded into the scale, the lazy rescale threshold tau and the
-//     causal tile skipping are those of the 32-query kernel.
+// The check must come before any P V product reads the tile's probabilities, so the
+// tiles run in a three-stage pipeline: iteration j issues the S^T MFMAs of tile j+2,
+// the P V MFMAs of tile j, and in between them the whole softmax of tile j+1, whose
+// sums are checked at the end of the iteration; its P V products run in the next.
+//
+// gfx950 mapping: K and V tiles are copied HBM -> LDS by buffer_load_dwordx4 ... lds
+// (no register staging) into a ring of R slots each; S^T = K Q^T and
+// O^T = V^T P^T on v_mfma_f32_32x32x16_{bf16,f16}, each lane owning one query column,
+// the S^T accumulator rounded to 16 bits is the B operand of P V (key rows enter with
+// bits 2 and 3 of the row index swapped); XOR-swizzled LDS rows, transposed V reads
+// (ds_read_b64_tr_b16), exp2 with log2(e) folded into the scale; fenced MFMA slots,
+// each issuing one MFMA and then the work that runs while the matrix core executes it.
 #pragma once
 
 #include "fa_common.hpp"
 
 #ifndef FA_W_PF
-#define FA_W_PF 2         // MFMA steps an LDS operand read runs ahead
+#define FA_W_PF 2  // MFMA steps an LDS operand read runs ahead
 #endif
-#ifndef FA_W_KPRE
-#define FA_W_KPRE 1       // first K operands of a tile read at the end of the previous one
-#endif
-#ifndef FA_W_PAIRS_B128
-#define FA_W_PAIRS_B128 19  // score pairs (of 32) exponentiated in the S^T block, d = 128
-#endif
-#ifndef FA_W_PAIRS_B64
-#define FA_W_PAIRS_B64 18   // the same for d = 64
-#endif
-#define FA_W_PAIRS_B(D) ((D) == 128 ? FA_W_PAIRS_B128 : FA_W_PAIRS_B64)
 
 namespace fa {
 
@@ -74,26 +65,8 @@ struct WideGeom {
   static_assert(BC % 32 == 0 && CHUNKS % 64 == 0, "whole MFMA blocks and wave copies");
   static_assert(INSTR % NW == 0 && PER_WAVE >= 1, "every wave issues the same copies");
   static_assert(2 * PER_WAVE <= NQK, "copies fit in the S^T pipeline steps");
-  static_assert(R >= 2 && R % 2 == 0, "ring of an even number of slots");
-  static_assert(2 * PER_WAVE * (R - 1) <= 63, "outstanding copies fit the vmcnt field");
+  static_assert(R >= 4 && R % 2 == 0, "the ring holds the tiles of three stages");
 };
-
-// Checks the softmax schedule of the P V block: with the units of pairs ub/3 .. npair-1
-// spread evenly over `ces` slots, the last unit of every pair lands at least one slot
-// before the first MFMA that reads its P step (pairs npair/nst per step, steps of `db`
-// slot pairs).
-constexpr bool fa_wide_exp_deadlines(int npair, int nst, int db, int ub, int ces) {
-  const int uc = 3 * npair - ub;
-  if (uc == 0) return true;
-  if (ces <= 0 || ub % 3 != 0) return false;
-  for (int v = ub / 3; v < npair; ++v) {
-    const int rel = 3 * v + 2 - ub;
-    int slot = 0;
-    while ((slot + 1) * uc / ces <= rel) ++slot;  // slot s holds units [s uc/ces, (s+1) uc/ces)
-    if (slot > 2 * (v / (npair / nst)) * db - 2) return false;
-  }
-  return true;
-}
 
 // O~ += A B with the accumulator held in AGPRs (the S^T accumulators stay in VGPRs,
 // where the VALU reads them). Written out because the compiler picks one register
@@ -143,6 +116,77 @@ __device__ __forceinline__ float keep_if_le(float x, int c, int t) {
   return x;
 }
 
+
+// The softmax of one key tile, as a stream of VALU instructions ("ops") placed into the
+// MFMA slots of an iteration. A lane holds NPAIR pairs of scores per tile; per pair, ops
+// 0-1 are the two exponent arguments s c - m (FMA), 2-3 their exponentials, 4-5 the two
+// adds into the tile sums, 6 the 16-bit pack into the P operand. The three stages of
+// consecutive pairs are staggered (step k holds the arguments of pair k, the
+// exponentials of pair k - LB and the sums and pack of pair k - LC), so an op never
+// reads the result of the op just before it. The ops go into the slots in stream order
+// such that the issue time of every slot (its ops plus its LDS reads and copies, in
+// half-cycles of measured issue cost) is as even as possible.
+template <int NPAIR, int NSLOT>
+struct OpSched {
+  int code[7 * NPAIR];  // 8 * pair + op
+  int first[NSLOT + 1]; // ops [first[s], first[s + 1]) go into slot s
+};
+template <int NPAIR, int NSLOT, int LB, int LC, int SC_N, int NQK, int NPV, int PF, int NDMA>
+constexpr OpSched<NPAIR, NSLOT> make_op_sched() {
+  OpSched<NPAIR, NSLOT> t{};
+  int n = 0;
+  const int lag[3] = {0, LB, LC};
+  const int ops_of[3][4] = {{0, 1, -1, -1}, {2, 3, -1, -1}, {4, 5, 6, -1}};
+  for (int k = 0; k < NPAIR + LC; ++k)
+    for (int st = 0; st < 3; ++st) {
+      const int v = k - lag[st];
+      if (v < 0 || v >= NPAIR) continue;
+      for (int q = 0; q < 4 && ops_of[st][q] >= 0; ++q) t.code[n++] = 8 * v + ops_of[st][q];
+    }
+  // issue costs in half-cycles
+  const int op_cost[7] = {11, 11, 24, 24, 11, 11, 11};
+  int fixed[NSLOT] = {};
+  long total = 0;
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    int f = 4;  // the MFMA
+    if (sl < SC_N) {
+      const int i = sl / 2, qb = sl % 2;
+      if (i + PF < NPV) f += 8;                       // one transposed V read
+      if (qb == 0 && i >= NPV - PF) f += 8;           // a K read for the next block
+      if (sl % 2 == 1 && sl / 2 < NDMA) f += 18;      // an LDS copy and its M0 set-up
+    } else {
+      const int sb = sl - SC_N, i = sb / 2, qb = sb % 2;
+      if (qb == 0 && i + PF < NQK) f += 8;            // a K read
+      if (i >= NQK - PF) f += 8;                      // a V^T read for the next iteration
+    }
+    fixed[sl] = f;
+    total += f;
+  }
+  for (int i = 0; i < 7 * NPAIR; ++i) total += op_cost[t.code[i] % 8];
+  long cum = 0;
+  int o = 0;
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    t.first[sl] = o;
+    cum += fixed[sl];
+    const long target = total * (sl + 1) / NSLOT;
+    // take ops while that brings the running issue time closer to the target
+    while (o < 7 * NPAIR) {
+      const int c = op_cost[t.code[o] % 8];
+      if (cum + c <= target || (cum + c - target) < (target - cum)) {
+        cum += c;
+        ++o;
+      } else {
+        break;
+      }
+    }
+  }
+  t.first[NSLOT] = 7 * NPAIR;
+  return t;
+}
+template <int NPAIR, int NSLOT, int LB, int LC, int SC_N, int NQK, int NPV, int PF, int NDMA>
+constexpr OpSched<NPAIR, NSLOT> kOpSched =
+    make_op_sched<NPAIR, NSLOT, LB, LC, SC_N, NQK, NPV, PF, NDMA>();
+
 template <bool BF16, int D, bool CAUSAL, int BC, int R>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_fwd_wide_kernel(const Params p) {
@@ -150,36 +194,13 @@ fa_fwd_wide_kernel(const Params p) {
   using E = Elt<BF16>;
   constexpr int NW = G::NW, CPR = G::CPR, NQK = G::NQK, NPV = G::NPV, NST = G::NST;
   constexpr int CHUNKS = G::CHUNKS, PW = G::PER_WAVE, NDMA = 2 * PW;
-  // ---- pipeline schedule -----------------------------------------------------------
-  // Each tile runs as two blocks of MFMA slots: the S^T MFMAs of the next tile (block
-  // B), then the P V MFMAs of this tile (block C). A slot issues one MFMA and then a
-  // batch of other instructions (LDS operand reads, copies, softmax work) that the wave
-  // issues while the matrix core executes it; slots are fenced from each other, so two
-  // MFMAs are never issued back to back (the second would stall the wave for the whole
-  // first one) and the VALU work is spread evenly over the tile.
-  //
-  // A lane holds NPAIR pairs of scores per tile (both query blocks). The softmax work
-  // of pair v is three units: the two exponentials, then the accumulation into the
-  // running sums and the 16-bit packing of the P operand. The first PAIRS_B pairs are
-  // done in block B, the rest in block C, each at least one slot before the first P V
-  // MFMA that reads them. Block C also carries the row max of the next tile (one max3
-  // per pair) and, after it, the rescale vote.
-  constexpr int SB_N = 2 * NQK;                 // slots of block B
-  constexpr int SC_N = 2 * NPV;                 // slots of block C
+  constexpr int SB_N = 2 * NQK;                 // slots of the S^T block (tile j+2)
+  constexpr int SC_N = 2 * NPV;                 // slots of the P V block (tile j)
+  constexpr int NSLOT = SB_N + SC_N;
   constexpr int NPAIR = BC / 2;                 // score pairs per lane and tile
-  constexpr int PAIRS_B = FA_W_PAIRS_B(D) < NPAIR ? FA_W_PAIRS_B(D) : NPAIR;
-  constexpr int UB = 3 * PAIRS_B;               // softmax units in block B
-  constexpr int UC = 3 * NPAIR - UB;            // softmax units in block C
-  // block C carries them up to two slots before the first MFMA of the last P step
-  constexpr int C_EXP_SLOTS = 2 * (NST - 1) * (D / 32) - 1;
-  constexpr int M_SLOTS = SC_N - 3;             // max units; the vote is in the next slot
-  static_assert(PAIRS_B >= NPAIR / NST, "the first P step is complete before block C");
-  static_assert(fa_wide_exp_deadlines(NPAIR, NST, D / 32, UB, C_EXP_SLOTS),
-                "every P operand is complete one slot before the MFMA that reads it");
-  // K ring and V ring; slot u of a ring holds one tile at offset u * CHUNKS
+  static_assert(R >= 4 && R % 2 == 0, "the ring holds the tiles of three stages");
   __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
   __shared__ __attribute__((aligned(1024))) u32x4_t vbuf[R * CHUNKS];
-  // landing area of the L2-warming copies below (their data is never read)
   __shared__ __attribute__((aligned(1024))) u32x4_t warm[NW * 64];
 
   const int tid = threadIdx.x;
@@ -197,23 +218,16 @@ fa_fwd_wide_kernel(const Params p) {
   const uint16_t* __restrict__ vg = p.v + head;
 
   const int q0 = qt * G::BR;
-  // The workgroup's 256 queries are eight 32-query blocks; wave w owns blocks w and 7 - w
-  // (query block qb = 0, 1 of the wave), so under the causal mask the four waves end
-  // their rows within one key tile of each other.
+  // wave w owns the 32-query blocks w and 7 - w of the workgroup's 256 queries
   const int qbase[2] = {q0 + 32 * wid, q0 + 32 * (2 * NW - 1 - wid)};
-  const int wq0 = qbase[0];  // the wave's first query
+  const int wq0 = qbase[0];
   const int q_end = min(q0 + G::BR, N);
   const int n_kt = CAUSAL ? (q_end + BC - 1) / BC : (N + BC - 1) / BC;
   const bool wave_live = wq0 < N;
   const int w_last_q = min(qbase[1] + 32, N) - 1;
   const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
 
-  // ---- HBM -> LDS copies ---------------------------------------------------------
-  // Lane `lane` of copy instruction i writes LDS chunk 64 i + lane = (row, physical
-  // chunk) of a tile; it fetches the logical chunk that the swizzle puts there.
-  // Copy ii covers rows 64 NW ii / CPR further down than copy 0, a multiple of 16 rows,
-  // and both swizzles depend on the row only modulo 16: the byte offsets of copy ii
-  // are those of copy 0 plus II_BYTES * ii.
+  // ---- HBM -> LDS copies (see the two-stage kernel for the layout) ------------------
   constexpr uint32_t II_BYTES = NW * 64 * 16;
   static_assert((NW * 64 / CPR) % 16 == 0, "copies are whole 16-row groups");
   uint32_t koff, voff;
@@ -222,40 +236,34 @@ fa_fwd_wide_kernel(const Params p) {
     koff = (uint32_t)(row * D + (ph ^ swz_k<D>(row)) * 8) * 2u;
     voff = (uint32_t)(row * D + (ph ^ swz_v<D>(row)) * 8) * 2u;
   }
-  // One copy of tile j. The buffer resource spans the tile's rows below N, so chunks
-  // of rows past N read as zeros (their scores are masked to -inf). Tiles past the
-  // last are clamped to it: such a copy lands in a slot no later tile reads.
-  // The buffer of tile j spans its rows below N: the range check zero-fills the rest.
-  auto tile_rsrc = [&](const uint16_t* src, int j) {
-    const int k0 = min(j, n_kt - 1) * BC;
+  // the buffer of tile t spans its rows below N (the range check zero-fills the rest);
+  // tiles past the last are clamped to it
+  auto tile_rsrc = [&](const uint16_t* src, int t) {
+    const int k0 = min(t, n_kt - 1) * BC;
     return buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)k0 * D),
                        (uint32_t)(min(N - k0, BC) * D * 2));
   };
-  // LDS byte address of this wave's first chunk in slot 0 of each ring; the slot
-  // and copy offsets are immediates
   const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(kbuf + wid * 64));
   const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(vbuf + wid * 64));
-  struct Copies {
-    int k_slot, v_slot;
-    int jk, jv;
-  };
-  // copy step i of a tile: K copies first, then V copies
-  auto copy_step = [&](const Copies& cp, int i) {
+  // copy step i of tile kt (K, into ring slot ks) and tile vt (V, slot vs): K copies
+  // first, then V copies; the slots are compile-time constants after unrolling
+  auto copy_step = [&](int kt, int ks, int vt, int vs, int i) __attribute__((always_inline)) {
     if (i < PW)
-      lds_copy16(tile_rsrc(kg, cp.jk), koff + II_BYTES * i, k_lds,
-                 cp.k_slot * CHUNKS * 16 + i * NW * 1024);
+      lds_copy16(tile_rsrc(kg, kt), koff + II_BYTES * i, k_lds, ks * CHUNKS * 16 + i * NW * 1024);
     else if (i < NDMA)
-      lds_copy16(tile_rsrc(vg, cp.jv), voff + II_BYTES * (i - PW), v_lds,
-                 cp.v_slot * CHUNKS * 16 + (i - PW) * NW * 1024);
+      lds_copy16(tile_rsrc(vg, vt), voff + II_BYTES * (i - PW), v_lds,
+                 vs * CHUNKS * 16 + (i - PW) * NW * 1024);
   };
-  auto copy_all = [&](const Copies& cp) {
+  auto copy_k = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) copy_step(cp, i);
+    for (int i = 0; i < PW; ++i) copy_step(kt, kt % R, 0, 0, i);
+  };
+  auto copy_v = [&](int vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = PW; i < NDMA; ++i) copy_step(0, 0, vt, vt % R, i);
   };
 
-  // ---- Q fragments (B operands of S^T = K Q^T), in registers for the whole loop -----
-  // Issued before any copy, so the first wait for K_0 also covers them. Rows past N
-  // load row N-1: their columns are never stored.
+  // ---- Q fragments (B operands of S^T = K Q^T), in AGPRs for the whole loop ----------
   u32x4_t qf[2][D / 16];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -264,13 +272,15 @@ fa_fwd_wide_kernel(const Params p) {
     for (int ds = 0; ds < D / 16; ++ds)
       qf[qb][ds] = global_load16(qg + (size_t)qi * D + ds * 16 + hh * 8);
   }
-
-  // ---- prologue copies: K_0, then (K_t, V_{t-1}) for t = 1 .. R-1 ---------------------
-  // the same (K, V) pairing as the main loop, so one vmcnt formula serves both
-#pragma unroll
-  for (int i = 0; i < PW; ++i) copy_step(Copies{0, 0, 0, 0}, i);
-#pragma unroll
-  for (int t = 1; t < R; ++t) copy_all(Copies{t, t - 1, t, t - 1});
+  // prologue copies, in this order: K_0, K_1, V_0, K_2, V_1, K_3, V_2 (K_4 follows once
+  // every wave is done with K_0's slot)
+  copy_k(0);
+  copy_k(1);
+  copy_v(0);
+  copy_k(2);
+  copy_v(1);
+  copy_k(3);
+  copy_v(2);
 
   // ---- running state ---------------------------------------------------------------
   f32x16_t oacc[D / 32][2];
@@ -280,17 +290,13 @@ fa_fwd_wide_kernel(const Params p) {
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
-  float ms[2] = {0.f, 0.f};
-  float ls[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // per-lane running sums, two chains each
+  float ms[2] = {0.f, 0.f};                   // reference max per query block (log2 units)
+  float ls[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // running sums, two chains per query block
+  float ts[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // sums of the tile in the softmax stage
   const float c = p.c;
+  const float thr = __builtin_amdgcn_exp2f(p.tau);  // largest probability allowed
 
-  // ---- per-lane LDS read addresses (see the 32-query kernel for the bank analysis) --
-  // Absolute LDS byte addresses of slot 0, pinned in registers, so that the slot and
-  // step offsets (all below 64 KB) become the immediate offsets of the reads even
-  // when the ring itself lies above 64 KB.
-  // K: the row pitch is a multiple of 128 bytes and the swizzle acts on chunk bits
-  // only, so the address of step ds is that of step 0 with (2 ds) << 4 XORed in
-  // (the logical chunk 2 ds + hh enters the XOR linearly).
+  // ---- per-lane LDS read addresses (see the two-stage kernel) ------------------------
   uint32_t kaddr0;
   {
     const int row = key_of_row(l32);
@@ -310,22 +316,20 @@ fa_fwd_wide_kernel(const Params p) {
     }
   }
   typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
-  auto k_frag = [&](int slot, int i) {
+  auto k_frag = [&](int slot, int i) __attribute__((always_inline)) {
     const int kb = i % (BC / 32), ds = i / (BC / 32);
     return *(lds_u32x4_t*)(uintptr_t)((kaddr0 ^ (uint32_t)(ds << 5)) + slot * CHUNKS * 16 +
                                       kb * 32 * CPR * 16);
   };
-  // half h (keys 4h .. 4h+3 of each 8-key group) of the V^T operand of P V step i
-  auto v_half = [&](int slot, int i, int h) {
+  auto v_half = [&](int slot, int i, int h) __attribute__((always_inline)) {
     const int db = i % (D / 32), st = i / (D / 32);
     const uint32_t b = vaddr[db] + slot * CHUNKS * 16;
     return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                            (lds_s16x4_t*)(uintptr_t)(b + (16 * st + 4 * h) * CPR * 16)));
   };
 
-  // S^T accumulators of one key tile: [key block][query block]; score e of a lane's
-  // query column (0 <= e < BC/2) is register e % 16 of key block e / 16
   typedef f32x16_t STile[BC / 32][2];
+  typedef u32x4_t PTile[2][NST];  // P~ packed as P V operands: [query block][16-key step]
   auto zero = [](STile& s) {
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -334,7 +338,6 @@ fa_fwd_wide_kernel(const Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
   };
-  // S^T of a whole tile from K slot kst, without interleaved work
   auto qk_plain = [&](int kst, STile& s) {
     zero(s);
 #pragma unroll
@@ -346,21 +349,14 @@ fa_fwd_wide_kernel(const Params p) {
     }
   };
 
-  // -inf on keys past N and, under the causal mask, on keys after the query; only
-  // tiles that reach past N or cross the diagonal need it
-  auto mask = [&](STile& s, int j) {
+  // -inf on keys past N and, under the causal mask, on keys after the query; only tiles
+  // that reach past N or cross the diagonal need it
+  auto mask = [&](STile& s, int j) __attribute__((always_inline)) {
     const int k0 = j * BC;
     const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > wq0);
-    if (!masked) return;
-    // With key = k0 + 8 hh + c (c = 32 kb + key_of_reg(r, 0), a constant per register),
-    // a score is kept iff c <= t, where t is the last allowed key of the lane's query
-    // (below N, and not after the query under the causal mask) minus k0 + 8 hh: one
-    // compare against a per-lane value per register.
+    if (!masked || j >= w_kt) return;  // tiles past the wave's last one are never used
     const int base = k0 + 8 * hh;
-    // the compares are inline assembly, which the compiler's hazard tracking does
-    // not see: wait out the S^T MFMAs first (an 8-pass XDL result needs about a
-    // dozen wait states before a VALU access), taking the tile as operands so the
-    // compares stay behind the padding
+    // wait out the S^T MFMAs before the inline-assembly compares read their results
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]));
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -379,17 +375,52 @@ fa_fwd_wide_kernel(const Params p) {
     }
   };
 
-  // m_new = max(m_old, rowmax S); alpha = exp2(m_old - m_new) rescales l and O~ of one
-  // query block. The wave skips it when no row's max rose by more than tau (log2 units).
-  // The compiler does not know that the P V MFMAs (inline assembly) write O~, so it
-  // inserts no wait states before VALU accesses of O~: this pads them (an 8-pass
-  // XDL result needs about a dozen) and, by taking the accumulators as operands,
-  // keeps every such access after the padding.
+  // ---- softmax of one tile: the op stream of make_op_sched -----------------------------
+  // A pair's exponent arguments and exponentials wait in tq / pq (indexed by the pair,
+  // modulo the pairs in flight between the stages); the first pair of each query block
+  // assigns the tile sums, the others add to them. Results are pinned, so each op is
+  // computed in the slot that issues it.
+  constexpr int LB = 1, LC = 2, NTQ = LB + 1, NPQ = LC - LB + 1;
+  float tq[NTQ][2], pq[NPQ][2];
+#define FA_W_OPS kOpSched<NPAIR, NSLOT, LB, LC, SC_N, NQK, NPV, FA_W_PF, NDMA>
+  // op o of the stream: see make_op_sched
+  auto exp_op = [&](const STile& s, PTile& pt, int o) __attribute__((always_inline)) {
+    const int v = FA_W_OPS.code[o] / 8, op = FA_W_OPS.code[o] % 8;
+    const int qb = (v / 4) % 2, e = 8 * (v / 8) + 2 * (v % 4);
+    const int bt = v % NTQ, bp = v % NPQ;
+    if (op < 2) {
+      tq[bt][op] = __builtin_fmaf(s[(e + op) / 16][qb][(e + op) % 16], c, -ms[qb]);
+      asm volatile("" : "+v"(tq[bt][op]));
+    } else if (op < 4) {
+      // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
+      pq[bp][op - 2] = __builtin_amdgcn_exp2f(tq[bt][op - 2]);
+      asm volatile("" : "+v"(pq[bp][op - 2]));
+    } else if (op < 6) {
+      if (v == 0 || v == 4)  // first pair of its query block in the tile
+        ts[qb][op - 4] = pq[bp][op - 4];
+      else
+        ts[qb][op - 4] += pq[bp][op - 4];
+      asm volatile("" : "+v"(ts[qb][op - 4]));
+    } else {
+      uint32_t w = E::pack(pq[bp][0], pq[bp][1]);
+      asm volatile("" : "+v"(w));
+      pt[qb][e / 8][(e % 8) / 2] = w;
+    }
+  };
+  auto softmax_all = [&](const STile& s, PTile& pt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int o = 0; o < 7 * NPAIR; ++o) exp_op(s, pt, o);
+  };
+
+  // O~ in AGPRs is written by inline-assembly MFMAs the compiler does not track: pad
+  // before any VALU access (an 8-pass XDL result needs about a dozen wait states)
   auto drain_o = [&](int qb) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(oacc[0][qb]));
 #pragma unroll
     for (int db = 1; db < D / 32; ++db) asm volatile("" : "+a"(oacc[db][qb]));
   };
+  // m_new = max(m_old, rowmax) when some row of the wave's query block exceeds its
+  // reference by more than tau (need); alpha = exp2(m_old - m_new) rescales l and O~
   auto grow_max = [&](int qb, float mxs, uint64_t need) {
     if (need != 0) {
       const float ms_new = __builtin_fmaxf(ms[qb], mxs);
@@ -398,8 +429,6 @@ fa_fwd_wide_kernel(const Params p) {
       ls[qb][0] *= alpha;
       ls[qb][1] *= alpha;
       drain_o(qb);
-      // one 16-register block at a time (it passes through VGPRs), so the rescale
-      // needs few registers while both S^T tiles are live
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -409,161 +438,126 @@ fa_fwd_wide_kernel(const Params p) {
       }
     }
   };
-
-  u32x4_t pb[2][NST];  // P~ of the current tile, packed as P V operands
-
-  // Softmax unit u of the current tile (pair v = u / 3): units 3v and 3v+1 are the two
-  // exponentials of the pair, unit 3v+2 adds them to the running sums and packs them
-  // into the P operand. Pair v is scores e, e+1 (e = 8 (v / 8) + 2 (v % 4)) of query
-  // block (v / 4) % 2, i.e. the P operands are produced in the order the P V steps
-  // consume them (16-key step major, query block minor). Results are pinned, so each
-  // unit is computed in the slot that issues it.
-  float pe[2];  // the exponentials of the pair in flight
-  auto exp_unit = [&](const STile& s, int u) {
-    const int v = u / 3, k = u % 3, qb = (v / 4) % 2, e = 8 * (v / 8) + 2 * (v % 4);
-    if (k < 2) {
-      // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
-      pe[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[(e + k) / 16][qb][(e + k) % 16], c, -ms[qb]));
-      asm volatile("" : "+v"(pe[k]));
-    } else {
-      ls[qb][0] += pe[0];
-      ls[qb][1] += pe[1];
-      uint32_t w = E::pack(pe[0], pe[1]);
-      asm volatile("" : "+v"(w), "+v"(ls[qb][0]), "+v"(ls[qb][1]));
-      pb[qb][e / 8][(e % 8) / 2] = w;
+  auto row_max = [&](const STile& s, int qb) {
+    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        m0 = __builtin_fmaxf(m0, __builtin_fmaxf(s[kb][qb][r], s[kb][qb][r + 1]));
+        m1 = __builtin_fmaxf(m1, __builtin_fmaxf(s[kb][qb][r + 2], s[kb][qb][r + 3]));
+      }
+    return xhalf_max(__builtin_fmaxf(m0, m1)) * c;
+  };
+  // The tile in the softmax stage may hold a probability above 2^tau (some lane's tile
+  // sum exceeds it): take its row max, raise the references that the rule raises, and
+  // recompute the tile's softmax against them.
+  auto fix_tile = [&](const STile& s, PTile& pt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float mx = row_max(s, qb);
+      grow_max(qb, mx, __builtin_amdgcn_ballot_w64(mx > ms[qb] + p.tau));
+    }
+    softmax_all(s, pt);
+  };
+  // Tile sums checked: all at most 2^tau, or the tile is fixed. Then they join l.
+  auto settle = [&](const STile& s, PTile& pt) __attribute__((always_inline)) {
+    const float big = __builtin_fmaxf(__builtin_fmaxf(ts[0][0], ts[0][1]),
+                                      __builtin_fmaxf(ts[1][0], ts[1][1]));
+    if (__builtin_amdgcn_ballot_w64(!(big <= thr)) != 0) fix_tile(s, pt);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      ls[qb][0] += ts[qb][0];
+      ls[qb][1] += ts[qb][1];
     }
   };
-  // Row max unit w of the next tile: one max3 over a pair of its scores, into one of two
-  // chains per query block.
-  auto max_unit = [&](const STile& s, float (&m)[2][2], int w) {
-    const int qb = w / (NPAIR / 2), k = w % (NPAIR / 2), e = 2 * k;
-    m[qb][k % 2] = __builtin_fmaxf(m[qb][k % 2], __builtin_fmaxf(s[e / 16][qb][e % 16],
-                                                                   s[e / 16][qb][(e + 1) % 16]));
-    asm volatile("" : "+v"(m[qb][k % 2]));
-  };
 
-  // Block B: S^T of tile j+1, slot 2i + qb = step i (key block i % (BC/32), head-dim
-  // slice i / (BC/32)) for query block qb. Besides its share of the softmax units of tile
-  // j, a slot carries the K operand read for FA_W_PF steps later (after the first MFMA
-  // of a step), this wave's copies of later tiles (one every SB_N / NDMA slots, so the
-  // four waves do not queue their copies at once) and, in the last steps, the first V^T
-  // operand reads of block C.
-  static_assert(SB_N % NDMA == 0, "copies spread evenly over block B");
-  u32x4_t kpre[FA_W_PF];  // the first K operands of the next block B
-  auto block_b = [&](int k_next, STile& s_next, const STile& s_cur, const Copies& cp,
-                     int v_cur, u32x2_t (&vpre)[FA_W_PF][2]) {
-    zero(s_next);
+  // ---- one iteration: P V of tile j, softmax of tile j+1, S^T of tile j+2 -------------
+  // Slots 0 .. SC_N-1 issue the P V MFMAs (step i = slot / 2: head-dim block i % (D/32),
+  // 16-key step i / (D/32); query block slot % 2), slots SC_N .. NSLOT-1 the S^T MFMAs
+  // (step i: key block i % (BC/32), head-dim slice i / (BC/32)). P V first: the P tile
+  // it consumes dies while the next one is produced, and the S^T tile it produces is
+  // born after half the softmax tile has been consumed, which keeps the live registers
+  // down. The softmax ops of tile j+1 are spread over all slots. LDS operand
+  // reads run FA_W_PF steps ahead: the first K operands of the S^T block are read in the
+  // last P V slots, the first V^T operands of the next iteration in the last S^T slots
+  // (from a slot no copy of the next iteration touches). This wave's copies of K_{j+R+1}
+  // and V_{j+R-1} (into the slots of K_{j+1} and V_{j-1}, both read in the previous
+  // iteration) go into every second slot of the P V block, early in the iteration: a V
+  // tile is first read at the end of the iteration after next, so it has nearly two
+  // iterations to land.
+  // On a wave's last tile the softmax stage works on a stale tile and its results are
+  // dropped (no branch inside the slots).
+  constexpr int COPY_EVERY = 2;
+  static_assert(COPY_EVERY * NDMA <= SC_N, "copies spread over the P V block");
+  u32x4_t vq[FA_W_PF];  // the first V^T operands of the next P V block
+  auto iteration = [&](int u, int j, STile& s_new, const STile& s_mid, PTile& p_mid,
+                       const PTile& p_cur) __attribute__((always_inline)) {
+    // ring slots: tile t is in slot t % R, and j % R = u
+    const int vst = u, kst = (u + 2) % R, vnext = (u + 1) % R;
+    u32x4_t vf[NPV];
     u32x4_t kf[NQK];
 #pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) kf[i] = FA_W_KPRE ? kpre[i] : k_frag(k_next, i);
+    for (int i = 0; i < FA_W_PF; ++i) vf[i] = vq[i];
 #pragma unroll
-    for (int sl = 0; sl < SB_N; ++sl) {
-      const int i = sl / 2, qb = sl % 2, kb = i % (BC / 32), ds = i / (BC / 32);
-      s_next[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_next[kb][qb]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(k_next, i + FA_W_PF);
-      if (sl % (SB_N / NDMA) == 1) copy_step(cp, sl / (SB_N / NDMA));
-      if (i >= NQK - FA_W_PF) vpre[i - (NQK - FA_W_PF)][qb] = v_half(v_cur, i - (NQK - FA_W_PF), qb);
-#pragma unroll
-      for (int u = sl * UB / SB_N; u < (sl + 1) * UB / SB_N; ++u) exp_unit(s_cur, u);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Block C: P V of tile j, slot 2i + qb = step i (head-dim block i % (D/32), P step
-  // i / (D/32)) for query block qb. A slot carries one half of the V^T operand read for
-  // FA_W_PF steps later, the remaining softmax units of tile j (up to two slots before
-  // their P step is read), the row max of tile j+1 and, in slot M_SLOTS, the exchange
-  // of the maxima between the two wave halves and the wave's rescale votes. Returns the
-  // row maxima of the two query blocks of tile j+1 (log2 units) and the votes.
-  // The last slots, which read no V^T operands, read the first K operands of the next
-  // tile's block B (K slot k_after), so that block starts without an LDS wait.
-  static_assert(2 * (NPV - FA_W_PF) + 2 * FA_W_PF <= SC_N, "slots for the K look-ahead");
-  auto block_c = [&](int v_cur, int k_after, const STile& s_cur, const STile& s_next,
-                     const u32x2_t (&vpre)[FA_W_PF][2], float& mx0, float& mx1, uint64_t& need0,
-                     uint64_t& need1) {
-    float m[2][2] = {{-__builtin_inff(), -__builtin_inff()},
-                     {-__builtin_inff(), -__builtin_inff()}};
-    u32x2_t vh[NPV][2];
-#pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) {
-      vh[i][0] = vpre[i][0];
-      vh[i][1] = vpre[i][1];
-    }
-#pragma unroll
-    for (int sl = 0; sl < SC_N; ++sl) {
-      const int i = sl / 2, qb = sl % 2, db = i % (D / 32), st = i / (D / 32);
-      // The compiler does not know the MFMAs below read their sources over several
-      // cycles (they are inline assembly): keep the previous step's sources live
-      // until this step, so no result is written into them right behind the MFMA.
+    for (int sc = 0; sc < SC_N; ++sc) {
+      const int i = sc / 2, qb = sc % 2, db = i % (D / 32), st = i / (D / 32);
+      // keep the previous step's sources live until this step (the inline-assembly
+      // MFMAs read them over several cycles)
       if (qb == 0 && i > 0)
-        asm volatile("" ::"v"(vh[i - 1][0]), "v"(vh[i - 1][1]), "v"(pb[0][(i - 1) / (D / 32)]),
-                     "v"(pb[1][(i - 1) / (D / 32)]));
-      const u32x4_t vf = {vh[i][0][0], vh[i][0][1], vh[i][1][0], vh[i][1][1]};
-      mfma_acc_agpr<BF16>(oacc[db][qb], vf, pb[qb][st]);
+        asm volatile("" ::"v"(vf[i - 1]), "v"(p_cur[0][(i - 1) / (D / 32)]),
+                     "v"(p_cur[1][(i - 1) / (D / 32)]));
+      mfma_acc_agpr<BF16>(oacc[db][qb], vf[i], p_cur[qb][st]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + FA_W_PF < NPV) vh[i + FA_W_PF][qb] = v_half(v_cur, i + FA_W_PF, qb);
-      if (FA_W_KPRE && qb == 0 && i >= NPV - FA_W_PF) kpre[i - (NPV - FA_W_PF)] = k_frag(k_after, i - (NPV - FA_W_PF));
-      if (sl < C_EXP_SLOTS) {
+      if (i + FA_W_PF < NPV) {
+        const u32x2_t h = v_half(vst, i + FA_W_PF, qb);
+        vf[i + FA_W_PF][2 * qb] = h[0];
+        vf[i + FA_W_PF][2 * qb + 1] = h[1];
+      }
+      if (qb == 0 && i >= NPV - FA_W_PF) kf[i - (NPV - FA_W_PF)] = k_frag(kst, i - (NPV - FA_W_PF));
+      if (sc % COPY_EVERY == 1)
+        copy_step(j + R + 1, (u + 1) % R, j + R - 1, (u + R - 1) % R, sc / COPY_EVERY);
 #pragma unroll
-        for (int u = sl * UC / C_EXP_SLOTS; u < (sl + 1) * UC / C_EXP_SLOTS; ++u)
-          exp_unit(s_cur, UB + u);
-      }
-      if (sl < M_SLOTS) {
-#pragma unroll
-        for (int w = sl * NPAIR / M_SLOTS; w < (sl + 1) * NPAIR / M_SLOTS; ++w)
-          max_unit(s_next, m, w);
-      }
-      if (sl == M_SLOTS) {
-        mx0 = xhalf_max(__builtin_fmaxf(m[0][0], m[0][1])) * c;
-        mx1 = xhalf_max(__builtin_fmaxf(m[1][0], m[1][1])) * c;
-        need0 = __builtin_amdgcn_ballot_w64(mx0 > ms[0] + p.tau);
-        need1 = __builtin_amdgcn_ballot_w64(mx1 > ms[1] + p.tau);
-        asm volatile("" : "+v"(mx0), "+v"(mx1), "+s"(need0), "+s"(need1));
-      }
+      for (int o = FA_W_OPS.first[sc]; o < FA_W_OPS.first[sc + 1]; ++o) exp_op(s_mid, p_mid, o);
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-  // One key tile j whose masked S^T is in s_cur and whose max is already folded into
-  // ms: exponentials and P V of tile j, overlapped with the S^T, mask and max of tile
-  // j+1 (from K slot k_next). On a wave's last tile the look-ahead reads a slot that
-  // holds a stale or clamped tile, and its result is dropped (`next` false).
-  auto tile = [&](const STile& s_cur, STile& s_next, int k_next, int v_cur, int k_after, int j,
-                  bool next, const Copies& cp) {
-    u32x2_t vpre[FA_W_PF][2];
-    block_b(k_next, s_next, s_cur, cp, v_cur, vpre);
-    mask(s_next, j + 1);
-    float mx0, mx1;
-    uint64_t need0, need1;
-    block_c(v_cur, k_after, s_cur, s_next, vpre, mx0, mx1, need0, need1);
-    if (next) {
-      grow_max(0, mx0, need0);
-      grow_max(1, mx1, need1);
+    asm volatile("" ::"v"(vf[NPV - 1]), "v"(p_cur[0][NST - 1]), "v"(p_cur[1][NST - 1]));
+    zero(s_new);
+#pragma unroll
+    for (int sb = 0; sb < SB_N; ++sb) {
+      const int sl = SC_N + sb;
+      const int i = sb / 2, qb = sb % 2, kb = i % (BC / 32), ds = i / (BC / 32);
+      s_new[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_new[kb][qb]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(kst, i + FA_W_PF);
+      if (i >= NQK - FA_W_PF) {
+        const u32x2_t h = v_half(vnext, i - (NQK - FA_W_PF), qb);
+        vq[i - (NQK - FA_W_PF)][2 * qb] = h[0];
+        vq[i - (NQK - FA_W_PF)][2 * qb + 1] = h[1];
+      }
+#pragma unroll
+      for (int o = FA_W_OPS.first[sl]; o < FA_W_OPS.first[sl + 1]; ++o) exp_op(s_mid, p_mid, o);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    mask(s_new, j + 2);
   };
 
-  // After this wave's copies for tiles up to (K_{j+2}, V_{j+1}) have landed (and
-  // K_{j+3}, whose first operands the next tile reads ahead), the newest RING_LAG
-  // iterations of copies may still be in flight.
-  constexpr int RING_LAG = FA_W_KPRE ? R - 3 : R - 2;
-  static_assert(RING_LAG >= 0, "ring deep enough for the K look-ahead");
-  auto wait_ring = [&]() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * RING_LAG) : "memory");
-  };
-  // Workgroup barrier for the ring. This wave's LDS reads are complete before it
-  // (lgkmcnt), so after it another wave may overwrite the slots they read; copies
-  // are ordered by the explicit vmcnt waits. The memory clobber keeps LDS accesses
-  // and copies on their side of it. (A full __syncthreads fence would also wait for
-  // the copies still in flight, which the ring is there to avoid.)
+  // ---- ring waits and barriers --------------------------------------------------------
+  // At the end of iteration j every copy but this iteration's must have landed (the next
+  // iteration reads K_{j+3}, V_{j+1}, and at its end V_{j+2}), and the barrier must follow
+  // this wave's last K read (the 2 FA_W_PF V^T reads for the next iteration issued
+  // after it may stay in flight: no copy of the next iteration goes into their slot).
+  auto end_wait = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory"); };
   auto ring_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  auto loop_barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(2 * FA_W_PF) : "memory");
+  };
 
-  // ---- S^T of tile 0 and the initial reference max ------------------------------------
+  // ---- prologue: S^T and softmax of tile 0, S^T of tile 1 -----------------------------
   STile sa, sb;
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * (R - 1)) : "memory");  // Q and K_0
-  // Q has landed: sign flip for a negative scale, then Q lives in AGPRs (MFMA source
-  // operands may come from either register file), leaving the VGPRs to the S^T
-  // tiles and the VALU work
+  PTile pa, pb;
+  // Q, K_0 and K_1 have landed (the 5 copy groups issued after K_1 may be in flight)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * PW) : "memory");
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -577,39 +571,51 @@ fa_fwd_wide_kernel(const Params p) {
     qk_plain(0, sa);
     mask(sa, 0);
 #pragma unroll
+    for (int qb = 0; qb < 2; ++qb) ms[qb] = row_max(sa, qb);  // tile 0 holds key 0: finite
+    // S^T of tile 1 with the softmax of tile 0 in its slots
+    zero(sb);
+    u32x4_t kf[NQK];
+#pragma unroll
+    for (int i = 0; i < FA_W_PF; ++i) kf[i] = k_frag(1, i);
+#pragma unroll
+    for (int sl = 0; sl < SB_N; ++sl) {
+      const int i = sl / 2, qb = sl % 2, kb = i % (BC / 32), ds = i / (BC / 32);
+      sb[kb][qb] = E::mfma(kf[i], qf[qb][ds], sb[kb][qb]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(1, i + FA_W_PF);
+#pragma unroll
+      for (int o = 7 * NPAIR * sl / SB_N; o < 7 * NPAIR * (sl + 1) / SB_N; ++o) exp_op(sa, pa, o);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mask(sb, 1);
+#pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sa[kb][qb][r]);
-      // tile 0 holds key 0, allowed for every row: finite
-      ms[qb] = xhalf_max(mx) * c;
+      ls[qb][0] = ts[qb][0];
+      ls[qb][1] = ts[qb][1];
     }
   }
-  wait_ring();  // K_1 and V_0 (and K_2, V_1 with the K look-ahead)
-  ring_barrier();  // and every wave is done with slot 0 of K before K_R overwrites it
-  if (FA_W_KPRE) {
+  // every wave is done with K_0's slot before K_R goes into it
+  ring_barrier();
+  copy_k(R);
+  // everything but K_R has landed: K_2 .. K_{R-1}, V_0 .. V_2
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PW) : "memory");
+  ring_barrier();
 #pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) kpre[i] = k_frag(1, i);  // tile 0's block B: K_1
-  }
+  for (int i = 0; i < FA_W_PF; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x2_t x = v_half(0, i, h);
+      vq[i][2 * h] = x[0];
+      vq[i][2 * h + 1] = x[1];
+    }
 
-  // ---- warming the L2 for the next workgroup --------------------------------------------
-  // The hardware starts workgroup b + next_stride (the next round, same XCD, hence the
-  // same L2) when a workgroup of this round ends, and every workgroup of a round would
-  // fetch its 64 KB of Q from HBM at the same moment. So three tiles before its end this
-  // workgroup copies that Q tile, and the first K tile of its head (the next workgroup
-  // waits for both before its first MFMA), through the L2 into a scratch area of LDS;
-  // the next workgroup then finds them in the cache. The copies join the ring's memory
-  // counter: the waits of that iteration and the next leave them in flight as well.
-  constexpr int WARM_Q = D / 8;   // 64 rows of Q per wave, 1 KB per copy
-  constexpr int WARM_K = D / 32;  // 16 rows of K_0 per wave
+  // ---- L2 warming for the next workgroup (see the two-stage kernel) ------------------
+  constexpr int WARM_Q = D / 8;
+  constexpr int WARM_K = D / 32;
   constexpr int WARM_OPS = WARM_Q + WARM_K;
   const int next_item = p.next_stride > 0 ? (int)blockIdx.x + p.next_stride : -1;
   const bool do_warm = next_item >= 0 && next_item < p.n_qt * p.BH && n_kt >= 4;
   const int j_warm = n_kt - 3;
-  // buffer over `rows` rows of src from row r0 (rows past N read as zeros), wave-uniform:
-  // read from the first lane so it stays in scalar registers
   auto rows_rsrc = [&](const uint16_t* src, int r0, int rows) {
     const u32x4_t r4 = buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)min(r0, N - 1) * D),
                                    (uint32_t)(max(min(N - r0, rows), 0) * D * 2));
@@ -618,54 +624,51 @@ fa_fwd_wide_kernel(const Params p) {
                    (uint32_t)__builtin_amdgcn_readfirstlane(r4[2]),
                    (uint32_t)__builtin_amdgcn_readfirstlane(r4[3])};
   };
-  auto warm_next = [&]() {
+  auto warm_next = [&]() __attribute__((always_inline)) {
     int bh2, qt2;
     decode_tile<CAUSAL>(p, next_item, bh2, qt2);
     const size_t head2 = (size_t)bh2 * (size_t)N * D;
     const u32x4_t rq = rows_rsrc(p.q + head2, qt2 * G::BR + wid * 64, 64);
     const u32x4_t rk = rows_rsrc(p.k + head2, wid * (BC / NW), BC / NW);
     const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(warm + wid * 64));
-    const uint32_t off = (uint32_t)lane * 16u;  // 1 KB per copy: 64 lanes x 16 B
+    const uint32_t off = (uint32_t)lane * 16u;
 #pragma unroll
     for (int i = 0; i < WARM_Q; ++i) lds_copy16(rq, off + 1024u * i, lds, 0);
 #pragma unroll
     for (int i = 0; i < WARM_K; ++i) lds_copy16(rk, off + 1024u * i, lds, 0);
   };
-  static_assert(D * 2 * 64 == WARM_Q * 1024 && D * 2 * (BC / NW) == WARM_K * 1024,
-                "one wave's rows are whole 1 KB copies");
-  static_assert(NDMA * RING_LAG + WARM_OPS <= 63, "outstanding copies fit the vmcnt field");
+  static_assert(NDMA + WARM_OPS <= 63, "outstanding copies fit the vmcnt field");
 
-  // ---- main loop: slots of tile j are j % R (K and V), unrolled over the ring --------
+  // ---- main loop: iteration j = tile j's P V; unrolled over the ring -------------------
+  // S^T tiles alternate between sa and sb (tile t in sa when t is even), P tiles
+  // between pa and pb likewise; with R even, the parity of j is that of u.
   for (int j0 = 0; j0 < n_kt; j0 += R) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int j = j0 + u;
       if (j >= n_kt) break;
-      const Copies cp = {u, (u + R - 1) % R, j + R, j + R - 1};
-      STile& s_cur = (u % 2 == 0) ? sa : sb;
-      STile& s_nxt = (u % 2 == 0) ? sb : sa;
+      STile& s_mid = (u % 2 == 0) ? sb : sa;  // tile j+1
+      STile& s_new = (u % 2 == 0) ? sa : sb;  // tile j+2
+      PTile& p_cur = (u % 2 == 0) ? pa : pb;  // tile j
+      PTile& p_mid = (u % 2 == 0) ? pb : pa;  // tile j+1
       if (do_warm && j == j_warm) warm_next();
-      if (wave_live && j < w_kt)
-        tile(s_cur, s_nxt, (u + 1) % R, u, (u + 2) % R, j, j + 1 < w_kt, cp);
-      else
-        copy_all(cp);
+      if (wave_live && j < w_kt) {
+        iteration(u, j, s_new, s_mid, p_mid, p_cur);
+        if (j + 1 < w_kt) settle(s_mid, p_mid);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) copy_step(j + R + 1, (u + 1) % R, j + R - 1, (u + R - 1) % R, i);
+      }
       if (do_warm && (j == j_warm || j == j_warm + 1))
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA * RING_LAG + WARM_OPS) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA + WARM_OPS) : "memory");
       else
-        wait_ring();
-      ring_barrier();
+        end_wait();
+      loop_barrier();
     }
   }
-
-  // The last iterations' copies (of clamped tiles that no iteration reads) may still be
-  // in flight: let them land before the workgroup can end and its LDS be reassigned.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
-  // Under the causal mask the waves of a workgroup finish at different times: each
-  // stores its rows directly (8-byte pieces) as soon as it is done. Without the mask they
-  // finish together, and the rows go out through LDS as whole-row chunks (ai2048 +3%;
-  // the barrier this needs cost 1.5% on long causal runs).
   if constexpr (CAUSAL) {
     if (!wave_live) return;
     const float kLn2 = 0.69314718055994530942f;
@@ -691,12 +694,6 @@ fa_fwd_wide_kernel(const Params p) {
       }
     }
   } else {
-    // O leaves through LDS: each wave writes its 64 rows (the accumulator layout gives a
-    // lane 8 bytes of one row per write) into its own part of the K ring, then stores them
-    // as 16-byte chunks of whole rows (a store instruction covers 64 / CPR whole rows),
-    // instead of scattering 8-byte pieces over 32 rows per instruction. Chunk c of row r
-    // sits at chunk c ^ (r % CPR) of the row, so neither side conflicts on banks. The
-    // barrier makes every wave's last copies land before the ring is reused.
     static_assert(R * CHUNKS >= NW * 64 * CPR && (CPR & (CPR - 1)) == 0 && CPR <= 64,
                   "a 64-row O tile per wave fits the K ring");
     ring_barrier();
@@ -708,7 +705,7 @@ fa_fwd_wide_kernel(const Params p) {
       drain_o(qb);
       const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
       const float inv = 1.0f / l_tot;
-      const int rr = 32 * qb + l32;  // row of the wave's tile
+      const int rr = 32 * qb + l32;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -716,24 +713,25 @@ fa_fwd_wide_kernel(const Params p) {
           const f32x16_t& a = oacc[db][qb];
           const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
           const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-          const int c = db * 4 + g;  // 16-byte chunk of the row; this lane holds half hh
-          *reinterpret_cast<u32x2_t*>(ot + (rr * CPR + (c ^ (rr & (CPR - 1)))) * 16 + hh * 8) =
+          const int cc = db * 4 + g;
+          *reinterpret_cast<u32x2_t*>(ot + (rr * CPR + (cc ^ (rr & (CPR - 1)))) * 16 + hh * 8) =
               u32x2_t{w0, w1};
         }
       const int qi = qbase[qb] + l32;
       if (qi < N && hh == 0)
         p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int it = 0; it < CPR; ++it) {
-      const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
+      const int rr = (64 / CPR) * it + lane / CPR, cc = lane % CPR;
       const u32x4_t x =
-          *reinterpret_cast<const u32x4_t*>(ot + (rr * CPR + (c ^ (rr & (CPR - 1)))) * 16);
+          *reinterpret_cast<const u32x4_t*>(ot + (rr * CPR + (cc ^ (rr & (CPR - 1)))) * 16);
       const int qi = qbase[rr >> 5] + (rr & 31);
-      if (qi < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)qi * D + c * 8) = x;
+      if (qi < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)qi * D + cc * 8) = x;
     }
   }
 }
 
+#undef FA_W_OPS
 }  // namespace fa
