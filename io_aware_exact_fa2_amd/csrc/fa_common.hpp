@@ -28,7 +28,6 @@ struct Params {
   float c;        // |scale| * log2(e)
   uint32_t qsign; // 0x80008000 when scale < 0: Q is negated on load (exact), else 0
   float tau;      // rescale threshold in log2 units (fast kernel; 0: every tile)
-  int next_stride;  // > 0: workgroup b warms the L2 with the Q tile of workgroup b + next_stride
   // split-KV partial pass: keys [s * split_keys, (s + 1) * split_keys) for split s; the
   // normalized partial O (float32) and partial L of split s go to o_part / l_part
   int split_keys;

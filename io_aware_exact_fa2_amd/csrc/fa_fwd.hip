@@ -42,9 +42,6 @@ using fa_host::ranges_overlap;
 #ifndef FA_WIDE_RING
 #define FA_WIDE_RING 4    // LDS ring slots per tensor
 #endif
-#ifndef FA_WIDE_WARM
-#define FA_WIDE_WARM 1  // warm the L2 with the next round's Q tiles
-#endif
 #ifndef FA_WIDE_BC
 #define FA_WIDE_BC 64
 #endif
@@ -101,8 +98,6 @@ hipError_t launch_wide(fa::Params p, hipStream_t stream) {
   using G = fa::WideGeom<D, FA_WIDE_BC, FA_WIDE_RING>;
   p.n_qt = (p.N + G::BR - 1) / G::BR;
   const int grid = p.n_qt * p.BH;
-  // one workgroup per CU at a time: workgroup b + (CU count) is the next one on b's XCD
-  if (FA_WIDE_WARM) p.next_stride = cu_count();
   auto kern = fa::fa_fwd_wide_kernel<BF16, D, CAUSAL, FA_WIDE_BC, FA_WIDE_RING>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(G::NW * 64), 0, stream, p);
   return hipGetLastError();
@@ -136,7 +131,6 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
   p.tau = tau;
-  p.next_stride = 0;
   p.split_keys = 0;
   p.o_part = nullptr;
   p.l_part = nullptr;
@@ -258,7 +252,6 @@ int fa_splitkv_impl(const void* q, const void* k, const void* v, void* o, float*
   p.c = std::fabs(scale) * 1.4426950408889634f;
   p.qsign = std::signbit(scale) ? 0x80008000u : 0u;
   p.tau = FA_DEFAULT_RESCALE_LOG2;
-  p.next_stride = 0;
   p.split_keys = keys;
   const uint64_t rows = static_cast<uint64_t>(p.BH) * N;
   p.o_part = static_cast<float*>(ws);

@@ -201,7 +201,6 @@ fa_fwd_wide_kernel(const Params p) {
   static_assert(R >= 4 && R % 2 == 0, "the ring holds the tiles of three stages");
   __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
   __shared__ __attribute__((aligned(1024))) u32x4_t vbuf[R * CHUNKS];
-  __shared__ __attribute__((aligned(1024))) u32x4_t warm[NW * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -609,36 +608,6 @@ fa_fwd_wide_kernel(const Params p) {
       vq[i][2 * h + 1] = x[1];
     }
 
-  // ---- L2 warming for the next workgroup (see the two-stage kernel) ------------------
-  constexpr int WARM_Q = D / 8;
-  constexpr int WARM_K = D / 32;
-  constexpr int WARM_OPS = WARM_Q + WARM_K;
-  const int next_item = p.next_stride > 0 ? (int)blockIdx.x + p.next_stride : -1;
-  const bool do_warm = next_item >= 0 && next_item < p.n_qt * p.BH && n_kt >= 4;
-  const int j_warm = n_kt - 3;
-  auto rows_rsrc = [&](const uint16_t* src, int r0, int rows) {
-    const u32x4_t r4 = buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)min(r0, N - 1) * D),
-                                   (uint32_t)(max(min(N - r0, rows), 0) * D * 2));
-    return u32x4_t{(uint32_t)__builtin_amdgcn_readfirstlane(r4[0]),
-                   (uint32_t)__builtin_amdgcn_readfirstlane(r4[1]),
-                   (uint32_t)__builtin_amdgcn_readfirstlane(r4[2]),
-                   (uint32_t)__builtin_amdgcn_readfirstlane(r4[3])};
-  };
-  auto warm_next = [&]() __attribute__((always_inline)) {
-    int bh2, qt2;
-    decode_tile<CAUSAL>(p, next_item, bh2, qt2);
-    const size_t head2 = (size_t)bh2 * (size_t)N * D;
-    const u32x4_t rq = rows_rsrc(p.q + head2, qt2 * G::BR + wid * 64, 64);
-    const u32x4_t rk = rows_rsrc(p.k + head2, wid * (BC / NW), BC / NW);
-    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(warm + wid * 64));
-    const uint32_t off = (uint32_t)lane * 16u;
-#pragma unroll
-    for (int i = 0; i < WARM_Q; ++i) lds_copy16(rq, off + 1024u * i, lds, 0);
-#pragma unroll
-    for (int i = 0; i < WARM_K; ++i) lds_copy16(rk, off + 1024u * i, lds, 0);
-  };
-  static_assert(NDMA + WARM_OPS <= 63, "outstanding copies fit the vmcnt field");
-
   // ---- main loop: iteration j = tile j's P V; unrolled over the ring -------------------
   // S^T tiles alternate between sa and sb (tile t in sa when t is even), P tiles
   // between pa and pb likewise; with R even, the parity of j is that of u.
@@ -651,7 +620,6 @@ fa_fwd_wide_kernel(const Params p) {
       STile& s_new = (u % 2 == 0) ? sa : sb;  // tile j+2
       PTile& p_cur = (u % 2 == 0) ? pa : pb;  // tile j
       PTile& p_mid = (u % 2 == 0) ? pb : pa;  // tile j+1
-      if (do_warm && j == j_warm) warm_next();
       if (wave_live && j < w_kt) {
         iteration(u, j, s_new, s_mid, p_mid, p_cur);
         if (j + 1 < w_kt) settle(s_mid, p_mid);
@@ -659,41 +627,14 @@ fa_fwd_wide_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) copy_step(j + R + 1, (u + 1) % R, j + R - 1, (u + R - 1) % R, i);
       }
-      if (do_warm && (j == j_warm || j == j_warm + 1))
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA + WARM_OPS) : "memory");
-      else
-        end_wait();
+      end_wait();
       loop_barrier();
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
-  if constexpr (CAUSAL) {
-    if (!wave_live) return;
-    const float kLn2 = 0.69314718055994530942f;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      drain_o(qb);
-      const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
-      const int qi = qbase[qb] + l32;
-      if (qi < N) {
-        const float inv = 1.0f / l_tot;
-        uint16_t* orow = p.o + head + (size_t)qi * D;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int dcol = db * 32 + g * 8 + hh * 4;
-            const f32x16_t& a = oacc[db][qb];
-            const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
-            const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-            *reinterpret_cast<u32x2_t*>(orow + dcol) = u32x2_t{w0, w1};
-          }
-        if (hh == 0) p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      }
-    }
-  } else {
+  {
     static_assert(R * CHUNKS >= NW * 64 * CPR && (CPR & (CPR - 1)) == 0 && CPR <= 64,
                   "a 64-row O tile per wave fits the K ring");
     ring_barrier();
