@@ -43,15 +43,8 @@ def kernel_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_hbm_counters.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256_16") != kernel_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    rec = profile_record(workload)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
 def _launcher(w, leg="fwd"):
@@ -270,6 +263,203 @@ def summarize_hbm(workload, fetch_dir, write_dir, copy_mib, out_path, commands, 
     return rec
 
 
+SQ_PASS1 = ("GRBM_GUI_ACTIVE SQ_WAVES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA "
+            "SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE")
+SQ_PASS2 = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+            "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_SALU")
+N_XCD, N_SIMD = 8, 1024      # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+MFMA_FLOPS = 32768           # one v_mfma_f32_32x32x16 (16-bit inputs): 2*32*32*16
+
+
+def _is_kernel(name, path):
+    if path == "fa1":
+        return "fa_fwd_fa1" in name
+    if path == "bwd":
+        return "fa_bwd" in name
+    return "fa_fwd" in name and "fa1" not in name and "fp8" not in name
+
+
+def _kernel_stats(directory, path):
+    """(name, calls, average ns, min ns, max ns) of the kernel, from --stats output."""
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    for r in rows:
+        if _is_kernel(r["Name"], path):
+            return (r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                    float(r["MaxNs"]))
+    raise SystemExit(f"no {path} kernel in the kernel stats under {directory}")
+
+
+def _all_counters(directory, path):
+    """Mean per-dispatch value of every counter of a --pmc run, for the kernel."""
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if _is_kernel(r["Kernel_Name"], path):
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in sorted(acc.items())}
+
+
+def summarize_profile(workload, dirs, copy_mib, path="fwd", cmd_args="", out_dir=None):
+    """Write profiles/<stem>_<workload>_rocprof.md and _hbm_counters.json from five
+    rocprofv3 runs of the same bench.py command: --kernel-trace --stats, two --pmc
+    passes of SQ counters (SQ_PASS1, SQ_PASS2), FETCH_SIZE and WRITE_SIZE."""
+    import workloads
+
+    kt_dir, sq1_dir, sq2_dir, fetch_dir, write_dir = dirs
+    w = workloads.get(workload)
+    stem = "fa_fwd" if path == "fwd" else f"fa_{path}"
+    name, calls, avg, mn, mx = _kernel_stats(kt_dir, path)
+    c1 = _all_counters(sq1_dir, path)
+    c2 = _all_counters(sq2_dir, path)
+    bench_cmd = f"python -u bench.py --workload {w.name}{cmd_args}"
+    cmds = {
+        "kernel_trace": f"rocprofv3 --kernel-trace --stats -f csv -d <kt_dir> -o kt -- {bench_cmd}",
+        "sq_pass1": f"rocprofv3 --pmc {SQ_PASS1} -f csv -d <sq1_dir> -o p -- {bench_cmd}",
+        "sq_pass2": f"rocprofv3 --pmc {SQ_PASS2} -f csv -d <sq2_dir> -o p -- {bench_cmd}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d <fetch_dir> -o p -- {bench_cmd} "
+                 f"--calibrate-copy-mib {copy_mib}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d <write_dir> -o p -- {bench_cmd} "
+                 f"--calibrate-copy-mib {copy_mib}",
+        "summary": f"python bench.py --workload {w.name} --path {path} --summarize-profile "
+                   f"<kt_dir> <sq1_dir> <sq2_dir> <fetch_dir> <write_dir> "
+                   f"--calibrate-copy-mib {copy_mib}",
+    }
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    out_json = os.path.join(out_dir, f"{stem}_{w.name}_hbm_counters.json")
+    hbm = summarize_hbm(w.name, fetch_dir, write_dir, copy_mib, out_json,
+                        " ; ".join(cmds[k] for k in ("fetch", "write", "summary")), path)
+    work = (2.5 if path == "bwd" else 1.0) * w.flops()
+    secs = avg * 1e-9
+    tflops = work / secs / 1e12
+    clock = c1["GRBM_GUI_ACTIVE"] / N_XCD / secs
+    active = c1["GRBM_GUI_ACTIVE"] / N_XCD
+    mfma_per_simd = c1["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD
+    sq = {
+        "clock_GHz_under_load": clock / 1e9,
+        "mfma_busy_pct": 100 * mfma_per_simd / active,
+        "cycles_per_mfma": c1["SQ_VALU_MFMA_BUSY_CYCLES"] / c1["SQ_INSTS_MFMA"],
+        "mfma_insts": c1["SQ_INSTS_MFMA"],
+        "mfma_insts_expected": work / MFMA_FLOPS,
+        "valu_insts_per_mfma": c1["SQ_INSTS_VALU"] / c1["SQ_INSTS_MFMA"],
+        "lds_bank_conflict_cycles": c1["SQ_LDS_BANK_CONFLICT"],
+        "lds_bank_conflict_pct_of_lds_active": 100 * c1["SQ_LDS_BANK_CONFLICT"]
+        / max(c1["SQ_LDS_IDX_ACTIVE"], 1.0),
+        "issue_pct_of_wave_cycles": 100 * c2["SQ_ACTIVE_INST_ANY"] / c2["SQ_WAVE_CYCLES"],
+        "valu_issue_pct_of_wave_cycles": 100 * c2["SQ_ACTIVE_INST_VALU"] / c2["SQ_WAVE_CYCLES"],
+        "waitcnt_pct_of_wave_cycles": 100 * c2["SQ_WAIT_ANY"] / c2["SQ_WAVE_CYCLES"],
+        "wait_issue_pct_of_wave_cycles": 100 * c2["SQ_WAIT_INST_ANY"] / c2["SQ_WAVE_CYCLES"],
+        "mfma_valu_coexec_pct_of_mfma_busy": 100 * c2["SQ_VALU_MFMA_COEXEC_CYCLES"]
+        / c1["SQ_VALU_MFMA_BUSY_CYCLES"],
+    }
+    hbm.update({"kernel_trace": {"calls": calls, "average_ns": avg, "min_ns": mn, "max_ns": mx,
+                                 "tflops_at_average": tflops},
+                "sq": sq, "sq_counters": {**c1, **c2}, "commands_all": cmds})
+    with open(out_json, "w") as f:
+        json.dump(hbm, f, indent=1)
+    peak_clk = 256 * clock * 4096 / 1e12
+    hbm_gbs = hbm["hbm_bytes_per_launch"] / secs / 1e9
+    mask = "causal" if w.causal else "non-causal"
+    lines = [
+        f"# {stem} kernel, workload {w.name} — rocprofv3 summary", "",
+        f"Workload: {w.name} = B={w.B}, H={w.H}, N={w.N}, d={w.d}, {w.dtype}, {mask}, "
+        f"scale = 1/sqrt(d); seeded synthetic inputs from `workloads`.",
+        f"Kernel: `{name}`.",
+        f"Kernel source hash (bench.py `kernel_hash`): {hbm['kernel_source_sha256_16']}. "
+        "All commands run from the repository root; output directories are placeholders; "
+        "every figure below is computed from the five runs by the summary command.", "",
+        "## Kernel trace (`--kernel-trace --stats`)", "", "    " + cmds["kernel_trace"], "",
+        f"| calls | average ns | min ns | max ns | TFLOPS at average | % of 2500 TFLOPS |",
+        "|---|---|---|---|---|---|",
+        f"| {calls} | {avg:.0f} | {mn:.0f} | {mx:.0f} | {tflops:.1f} | {100 * tflops / 2500:.1f} |",
+        "", f"FLOPs per launch: {work:.4e} ({'2.5 x ' if path == 'bwd' else ''}4·B·H·N²·d"
+        f"{', halved for the causal mask' if w.causal else ''}).", "",
+        "## SQ / GRBM counters (two `--pmc` passes, mean per dispatch)", "",
+        "    " + cmds["sq_pass1"], "", "    " + cmds["sq_pass2"], "",
+        "| counter | mean per dispatch |", "|---|---|",
+    ]
+    lines += [f"| {k} | {v:.6g} |" for k, v in sorted({**c1, **c2}.items())]
+    lines += [
+        "", f"Derived ({N_XCD} XCDs, {N_SIMD} SIMDs, the kernel-trace average duration):",
+        f"* clock under load = GRBM_GUI_ACTIVE / {N_XCD} / kernel time = "
+        f"{clock / 1e9:.3f} GHz; the 16-bit MFMA peak at that clock is 256 CUs x 4096 "
+        f"flop/cycle = {peak_clk:.0f} TFLOPS, of which this launch reaches "
+        f"{100 * tflops / peak_clk:.1f}%",
+        f"* cycles per MFMA = SQ_VALU_MFMA_BUSY_CYCLES / SQ_INSTS_MFMA = {sq['cycles_per_mfma']:.1f}",
+        f"* MFMA busy per SIMD = {mfma_per_simd:.0f} cycles = {sq['mfma_busy_pct']:.1f}% "
+        "of the active cycles",
+        f"* MFMA instructions: FLOPs / 32768 = {sq['mfma_insts_expected']:.4g} expected, "
+        f"{sq['mfma_insts']:.4g} counted",
+        f"* VALU instructions per MFMA = {sq['valu_insts_per_mfma']:.2f}",
+        f"* LDS bank-conflict cycles = {sq['lds_bank_conflict_cycles']:.6g} "
+        f"({sq['lds_bank_conflict_pct_of_lds_active']:.3f}% of SQ_LDS_IDX_ACTIVE)",
+        f"* of the wave cycles: issuing {sq['issue_pct_of_wave_cycles']:.1f}% (VALU incl. MFMA "
+        f"issue {sq['valu_issue_pct_of_wave_cycles']:.1f}%), waiting on a counter (s_waitcnt) "
+        f"{sq['waitcnt_pct_of_wave_cycles']:.1f}%, waiting to issue "
+        f"{sq['wait_issue_pct_of_wave_cycles']:.1f}%; MFMA and VALU co-execute "
+        f"{sq['mfma_valu_coexec_pct_of_mfma_busy']:.1f}% of the MFMA-busy cycles", "",
+        "## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", "",
+        "    " + cmds["fetch"], "", "    " + cmds["write"], "", "    " + cmds["summary"], "",
+        f"Each counter is scaled by what it reads for a plain {copy_mib} MiB device copy "
+        "(torch float32 multiply, out of place) in the same run:", "",
+        f"| | kernel KiB/dispatch | copy KiB/dispatch ({copy_mib} MiB true) | scale |",
+        "|---|---|---|---|",
+        f"| FETCH_SIZE | {hbm['fetch_kib_per_dispatch']:.1f} | {hbm['copy_fetch_kib']:.1f} | "
+        f"{hbm['fetch_scale']:.3f} |",
+        f"| WRITE_SIZE | {hbm['write_kib_per_dispatch']:.1f} | {hbm['copy_write_kib']:.1f} | "
+        f"{hbm['write_scale']:.3f} |", "",
+        f"HBM bytes per launch = {hbm['hbm_bytes_per_launch'] / 1e6:.1f} MB; algorithmic "
+        f"(Q, K, V read once, O written once, 4 B of L per row) = "
+        f"{hbm['algorithmic_bytes_per_launch'] / 1e6:.1f} MB; ratio "
+        f"{hbm['traffic_over_algorithmic']:.3f}. At the average kernel time that is "
+        f"{hbm_gbs:.0f} GB/s of the 8000 GB/s HBM peak.", "",
+    ]
+    out_md = os.path.join(out_dir, f"{stem}_{w.name}_rocprof.md")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    return hbm
+
+
+def profile_record(workload: str, path: str = "fwd"):
+    """The committed counter summary of a workload, if it was taken on the current
+    kernel source; else None."""
+    stem = "fa_fwd" if path == "fwd" else f"fa_{path}"
+    fn = os.path.join(ROOT, "profiles", f"{stem}_{workload}_hbm_counters.json")
+    try:
+        with open(fn) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return rec
+
+
+def profile_fields(workload: str, ms: float):
+    """Per-config figures from the committed profile (HBM bytes and their rate at this
+    run's time, MFMA busy, LDS bank conflicts, clock under load), or a null marker."""
+    rec = profile_record(workload)
+    if rec is None:
+        return {"profile": None}
+    out = {"hbm_bytes_per_launch": round(rec["hbm_bytes_per_launch"]),
+           "hbm_GBps": round(rec["hbm_bytes_per_launch"] / (ms * 1e-3) / 1e9, 1),
+           "traffic_over_algorithmic": round(rec["traffic_over_algorithmic"], 3)}
+    sq = rec.get("sq")
+    if sq:
+        out.update({"mfma_busy_pct": round(sq["mfma_busy_pct"], 1),
+                    "lds_bank_conflict_cycles": sq["lds_bank_conflict_cycles"],
+                    "valu_insts_per_mfma": round(sq["valu_insts_per_mfma"], 2),
+                    "clock_GHz_under_load": round(sq["clock_GHz_under_load"], 3)})
+    out["profile"] = f"profiles/fa_fwd_{workload}_rocprof.md"
+    return out
+
+
+def device_peak():
+    """16-bit MFMA peak from the device's CU count and peak engine clock."""
+    import io_aware_exact_fa2_amd as fa
+
+    cus, khz = fa.fa_device_info(0)
+    return cus, khz, cus * khz * 1e3 * 4096 / 1e12
+
+
 def cpu_baseline(w, budget_s: float):
     """The float64 oracle on whole heads of the same workload until ~budget_s."""
     import numpy as np
@@ -323,7 +513,20 @@ def main(argv=None):
     ap.add_argument("--summarize-hbm", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 --pmc runs into profiles/ (no GPU work)")
     ap.add_argument("--commands", default="", help="commands recorded in the summary")
+    ap.add_argument("--summarize-profile", nargs=5,
+                    metavar=("KT_DIR", "SQ1_DIR", "SQ2_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/*_rocprof.md and *_hbm_counters.json from five "
+                         "rocprofv3 runs (no GPU work)")
+    ap.add_argument("--profile-args", default=" --cpu-budget 0 --also '' --backward '' "
+                    "--fp8 '' --steps 20 --warmup 3",
+                    help="bench.py arguments the profiled runs used (recorded)")
     a = ap.parse_args(argv)
+    if a.summarize_profile:
+        rec = summarize_profile(a.workload, a.summarize_profile, a.calibrate_copy_mib or 512,
+                                a.path, a.profile_args)
+        print(json.dumps({"workload": rec["workload"], "sq": rec["sq"],
+                          "traffic_over_algorithmic": rec["traffic_over_algorithmic"]}))
+        return 0
     if a.summarize_hbm:
         stem = "fa_fwd" if a.path == "fwd" else f"fa_{a.path}"
         out = os.path.join(ROOT, "profiles", f"{stem}_{a.workload}_hbm_counters.json")
@@ -359,6 +562,18 @@ def main(argv=None):
     traffic = measured_traffic(w.name)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": traffic}
+    cus, khz, peak_dev = device_peak()
+    peaks = {"published_tflops": PEAK_TFLOPS, "frac_published": round(tflops / PEAK_TFLOPS, 4),
+             "device_cus": cus, "device_clock_mhz": khz / 1e3,
+             "clock_derived_tflops": round(peak_dev, 1),
+             "frac_clock_derived": round(tflops / peak_dev, 4),
+             "formula": "CUs x peak engine clock x 4096 flop/cycle (hipDeviceProp_t)"}
+    prof = profile_fields(w.name, ms)
+    if prof.get("clock_GHz_under_load"):
+        ghz = prof["clock_GHz_under_load"]
+        peaks["clock_under_load_GHz"] = ghz
+        peaks["at_clock_under_load_tflops"] = round(cus * ghz * 1e9 * 4096 / 1e12, 1)
+        peaks["frac_at_clock_under_load"] = round(tflops / peaks["at_clock_under_load_tflops"], 4)
     ms_cold = time_cold(w, 10)
     cold = {"ms": round(ms_cold, 4), "tflops": round(w.flops() / (ms_cold * 1e-3) / 1e12, 1),
             "scrub_mib": 512, "statistic": "median of 10 launches, each after the scrub"}
@@ -368,8 +583,10 @@ def main(argv=None):
         msx, _, _ = time_gpu(wx, max(5, a.steps // 5), 3)
         tx = wx.flops() / (msx * 1e-3) / 1e12
         extra[name] = {"ms": round(msx, 4), "tflops": round(tx, 1),
-                       "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1), "dtype": wx.dtype,
-                       "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d]}
+                       "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1),
+                       "pct_clock_derived_peak": round(100 * tx / peak_dev, 1), "dtype": wx.dtype,
+                       "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d],
+                       **profile_fields(name, msx)}
     bwd = {}
     for name in [s for s in a.backward.split(",") if s]:
         wx = workloads.get(name)
@@ -386,7 +603,6 @@ def main(argv=None):
         tx = wx.flops() / (msx * 1e-3) / 1e12
         f8[name] = {"ms": round(msx, 4), "tflops": round(tx, 1),
                     "pct_fp8_peak": round(100 * tx / PEAK_FP8_TFLOPS, 1),
-                    "pct_bf16_peak": round(100 * tx / PEAK_TFLOPS, 1),
                     "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d],
                     "inputs": "E4M3 codes with per-tensor scales, bf16 O"}
     line = {
@@ -408,6 +624,8 @@ def main(argv=None):
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "scale": w.scale},
         "pct_bf16_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "peak": peaks,
+        "profile": prof,
         "algorithmic_GBps": round(w.min_bytes() / (ms * 1e-3) / 1e9, 1),
         "wall_s_timed": round(wall, 4),
         "kernel_source_sha256_16": kernel_hash(),

@@ -317,6 +317,18 @@ int fa_fwd_supported(int d, int dtype, int causal);
  */
 int fa_device_supported(int device);
 
+/*
+ * fa_device_info — compute-unit count and peak engine clock (kHz) of HIP device
+ * `device`, as the runtime reports them (hipDeviceProp_t multiProcessorCount and
+ * clockRate), so a caller can price a measured rate against the matrix-core peak of
+ * that device: CUs x clock x 4096 flops per cycle for 16-bit MFMA on gfx950 (four
+ * SIMDs, each finishing a 32x32x16 product, 32768 flops, every 32 cycles).
+ * Returns FA_OK, FA_ERR_NULL for a NULL output pointer, or FA_ERR_HIP (no such device,
+ * or the runtime failed; fa_last_hip_error() names it). Outputs are 0 on error.
+ * Launches nothing.
+ */
+int fa_device_info(int device, int* cu_count, int* clock_khz);
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* fa_strerror(int status);
 

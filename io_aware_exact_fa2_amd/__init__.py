@@ -23,7 +23,7 @@ __all__ = [
     "library_path", "lib", "fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_supported",
     "fa_bwd", "fa_bwd_fp16", "backward", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
     "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "forward_splitkv", "forward_fa1", "FA_MAX_SPLITS",
-    "fa_fwd_fp8", "forward_fp8", "fa_device_supported", "fa_fwd_splitkv_static",
+    "fa_fwd_fp8", "forward_fp8", "fa_device_supported", "fa_device_info", "fa_fwd_splitkv_static",
     "FA_ERR_SCRATCH", "FA_STATIC_SCRATCH_BYTES",
     "fa_strerror", "FA_DEFAULT_RESCALE_LOG2", "FA_MAX_RESCALE_LOG2",
     "fa_last_hip_error", "fa_version", "forward", "EXPORTS",
@@ -43,7 +43,7 @@ FA_DTYPE_FP16 = 1
 EXPORTS = ("fa_fwd", "fa_fwd_fp16", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
            "fa_fwd_splitkv_static",
            "fa_fwd_fa1", "fa_fwd_fa1_workspace_size", "fa_bwd", "fa_bwd_fp16", "fa_fwd_supported",
-           "fa_device_supported",
+           "fa_device_supported", "fa_device_info",
            "fa_strerror", "fa_last_hip_error", "fa_version")
 FA_MAX_SPLITS = 64
 FA_STATIC_SCRATCH_BYTES = 64 << 20
@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = i
     L.fa_device_supported.argtypes = [i]
     L.fa_device_supported.restype = i
+    L.fa_device_info.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.fa_device_info.restype = i
     L.fa_fwd_supported.argtypes = [i, i, i]
     L.fa_fwd_supported.restype = i
     L.fa_strerror.argtypes = [i]
@@ -209,6 +211,16 @@ def fa_bwd_fp16(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal,
 def fa_device_supported(device: int = 0) -> int:
     """C ``fa_device_supported``: 1 for a gfx950 device, else 0."""
     return lib().fa_device_supported(int(device))
+
+
+def fa_device_info(device: int = 0) -> tuple[int, int]:
+    """C ``fa_device_info``: (compute-unit count, peak engine clock in kHz) of a device;
+    raises FAError if the runtime cannot report them."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().fa_device_info(int(device), ctypes.byref(cus), ctypes.byref(khz))
+    if st != FA_OK:
+        raise FAError(st, "fa_device_info")
+    return cus.value, khz.value
 
 
 def fa_fwd_supported(d: int, dtype: int, causal: int) -> int:

@@ -99,6 +99,30 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+// Layout of an O tile staged in LDS on its way to HBM (rows of CPR 16-byte chunks, CPR
+// = 8 or 16). The writers are lanes that each hold 8 bytes (one half, hh) of chunk c of
+// row r, 32 rows per instruction; the readers take whole 16-byte chunks. Chunk c of row r
+// sits at chunk o_pos(r, c), and its two halves trade places there when o_swap(r, c)
+// is 1. Every 16 consecutive rows of one write then cover the 32 two-bank pairs of a
+// 128-byte bank window once (and the 32 rows the 64 pairs of 256 bytes), and every 8
+// (16) lanes of a read one row's chunks, so neither side conflicts on banks.
+template <int CPR> __device__ __forceinline__ int o_pos(int r, int c) {
+  return CPR == 16 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+}
+template <int CPR> __device__ __forceinline__ int o_swap(int r, int c) {
+  return CPR == 16 ? (((c ^ r) >> 3) ^ (r >> 4)) & 1 : (r ^ (r >> 4)) & 1;
+}
+// Byte offset in the staged tile of half hh of chunk c of row r.
+template <int CPR> __device__ __forceinline__ int o_half_off(int r, int c, int hh) {
+  return (r * CPR + o_pos<CPR>(r, c)) * 16 + ((hh ^ o_swap<CPR>(r, c)) << 3);
+}
+// Chunk c of row r read back from the staged tile in logical order.
+template <int CPR>
+__device__ __forceinline__ u32x4_t o_chunk_read(const unsigned char* t, int r, int c) {
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(t + (r * CPR + o_pos<CPR>(r, c)) * 16);
+  return o_swap<CPR>(r, c) ? u32x4_t{x[2], x[3], x[0], x[1]} : x;
+}
+
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

@@ -542,6 +542,25 @@ int fa_device_supported(int device) {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
 }
 
+int fa_device_info(int device, int* cu_count, int* clock_khz) {
+  if (cu_count == nullptr || clock_khz == nullptr) return FA_ERR_NULL;
+  *cu_count = 0;
+  *clock_khz = 0;
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e == hipSuccess && (device < 0 || device >= n)) e = hipErrorInvalidDevice;
+  hipDeviceProp_t prop;
+  if (e == hipSuccess) e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // leave no sticky error behind
+    g_last_hip_error = static_cast<int>(e);
+    return FA_ERR_HIP;
+  }
+  *cu_count = prop.multiProcessorCount;
+  *clock_khz = prop.clockRate;
+  return FA_OK;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";

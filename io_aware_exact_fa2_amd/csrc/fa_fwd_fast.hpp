@@ -444,8 +444,7 @@ fa_fwd_fast_kernel(const Params p) {
   // O leaves through LDS (the loop ended at a barrier after every copy landed, so the K
   // and V slots are idle): the wave writes its 32 rows into its own part of them (a lane
   // holds 8 bytes of one row per write) and stores 16-byte chunks of whole rows, instead
-  // of 8-byte pieces over 32 rows per store instruction. Chunk c of row r sits at chunk
-  // c ^ (r % CPR) of the row (no bank conflicts on either side).
+  // of 8-byte pieces over 32 rows per store instruction, in the o_pos / o_swap layout.
   static_assert(NW <= 4 && 2 * 32 * CPR <= G::CHUNKS, "two waves' O tiles fit one slot");
   unsigned char* ot = reinterpret_cast<unsigned char*>((wid < 2 ? ks0 : vs0) + (wid & 1) * 32 * CPR);
 #pragma unroll
@@ -456,16 +455,14 @@ fa_fwd_fast_kernel(const Params p) {
       const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
       const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
       const int c = db * 4 + g;  // 16-byte chunk of row l32; this lane holds half hh
-      *reinterpret_cast<u32x2_t*>(ot + (l32 * CPR + (c ^ (l32 & (CPR - 1)))) * 16 + hh * 8) =
-          u32x2_t{w0, w1};
+      *reinterpret_cast<u32x2_t*>(ot + o_half_off<CPR>(l32, c, hh)) = u32x2_t{w0, w1};
     }
   if (hh == 0 && qi < N) p.lse[(size_t)bh * N + qi] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
 #pragma unroll
   for (int it = 0; it < CPR / 2; ++it) {
     const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
-    const u32x4_t x =
-        *reinterpret_cast<const u32x4_t*>(ot + (rr * CPR + (c ^ (rr & (CPR - 1)))) * 16);
+    const u32x4_t x = o_chunk_read<CPR>(ot, rr, c);
     if (wq0 + rr < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)(wq0 + rr) * D + c * 8) = x;
   }
 }

@@ -655,8 +655,7 @@ fa_fwd_wide_kernel(const Params p) {
           const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
           const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
           const int cc = db * 4 + g;
-          *reinterpret_cast<u32x2_t*>(ot + (rr * CPR + (cc ^ (rr & (CPR - 1)))) * 16 + hh * 8) =
-              u32x2_t{w0, w1};
+          *reinterpret_cast<u32x2_t*>(ot + o_half_off<CPR>(rr, cc, hh)) = u32x2_t{w0, w1};
         }
       const int qi = qbase[qb] + l32;
       if (qi < N && hh == 0)
@@ -666,8 +665,7 @@ fa_fwd_wide_kernel(const Params p) {
 #pragma unroll
     for (int it = 0; it < CPR; ++it) {
       const int rr = (64 / CPR) * it + lane / CPR, cc = lane % CPR;
-      const u32x4_t x =
-          *reinterpret_cast<const u32x4_t*>(ot + (rr * CPR + (cc ^ (rr & (CPR - 1)))) * 16);
+      const u32x4_t x = o_chunk_read<CPR>(ot, rr, cc);
       const int qi = qbase[rr >> 5] + (rr & 31);
       if (qi < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)qi * D + cc * 8) = x;
     }

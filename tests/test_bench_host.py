@@ -1,0 +1,86 @@
+"""Host logic of bench.py: the one-GPU guard and the rocprofv3 summary arithmetic, on
+synthetic profiler output written here (no GPU)."""
+import csv
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+FA = "void fa::fa_fwd_wide_kernel<true, 128, false, 64, 4>(fa::Params)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, MulFunctor<float> >(int)"
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def _pmc(d, per_kernel):
+    rows = []
+    for kernel, counters in per_kernel.items():
+        for name, vals in counters.items():
+            rows += [[kernel, name, v] for v in vals]
+    _write(os.path.join(d, "host", "p_counter_collection.csv"),
+           ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_profile_summary_arithmetic(tmp_path):
+    """A launch of 125 us that counts 8 x 2.2e6 x 125e-6 ... GRBM cycles runs at 2.2 GHz;
+    MFMA busy, VALU per MFMA and the copy-calibrated HBM bytes follow from the counters."""
+    w = workloads.get("ai2048")
+    avg_ns = 125_000.0
+    grbm = 8 * 2.2e9 * avg_ns * 1e-9            # 2.2 GHz on all 8 XCDs
+    mfma = w.flops() / 32768
+    busy = 0.5 * (grbm / 8) * 1024              # half the active cycles on every SIMD
+    dirs = [str(tmp_path / n) for n in ("kt", "sq1", "sq2", "fetch", "write")]
+    _write(os.path.join(dirs[0], "host", "kt_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+            "StdDev"],
+           [[COPY, 3, 3000, 1000, 1, 900, 1100, 10],
+            [FA, 100, 100 * avg_ns, avg_ns, 99, avg_ns - 1e3, avg_ns + 1e3, 5]])
+    _pmc(dirs[1], {FA: {"GRBM_GUI_ACTIVE": [grbm, grbm], "SQ_WAVES": [2048],
+                        "SQ_BUSY_CYCLES": [1.0], "SQ_VALU_MFMA_BUSY_CYCLES": [busy],
+                        "SQ_INSTS_MFMA": [mfma], "SQ_INSTS_VALU": [6 * mfma],
+                        "SQ_INSTS_LDS": [1.0], "SQ_LDS_BANK_CONFLICT": [0.0],
+                        "SQ_LDS_IDX_ACTIVE": [1e6]}})
+    _pmc(dirs[2], {FA: {"SQ_WAVE_CYCLES": [100.0], "SQ_WAIT_ANY": [20.0],
+                        "SQ_WAIT_INST_ANY": [10.0], "SQ_ACTIVE_INST_ANY": [70.0],
+                        "SQ_ACTIVE_INST_VALU": [50.0], "SQ_ACTIVE_INST_LDS": [5.0],
+                        "SQ_VALU_MFMA_COEXEC_CYCLES": [busy / 4], "SQ_INSTS_SALU": [1.0]}})
+    # the copy of 512 MiB reads half (fetch counter in 64-byte units of 32 B ...): scale 2
+    _pmc(dirs[3], {FA: {"FETCH_SIZE": [50_000.0]}, COPY: {"FETCH_SIZE": [512 * 1024 / 2]}})
+    _pmc(dirs[4], {FA: {"WRITE_SIZE": [30_000.0]}, COPY: {"WRITE_SIZE": [512 * 1024.0]}})
+    out = tmp_path / "out"
+    out.mkdir()
+    rec = bench.summarize_profile("ai2048", dirs, 512, out_dir=str(out))
+    sq = rec["sq"]
+    assert sq["clock_GHz_under_load"] == pytest.approx(2.2)
+    assert sq["mfma_busy_pct"] == pytest.approx(50.0)
+    assert sq["cycles_per_mfma"] == pytest.approx(busy / mfma)
+    assert sq["valu_insts_per_mfma"] == pytest.approx(6.0)
+    assert sq["mfma_insts_expected"] == pytest.approx(mfma)
+    assert sq["waitcnt_pct_of_wave_cycles"] == pytest.approx(20.0)
+    assert sq["mfma_valu_coexec_pct_of_mfma_busy"] == pytest.approx(25.0)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx((2 * 50_000.0 + 30_000.0) * 1024)
+    assert rec["traffic_over_algorithmic"] == pytest.approx(
+        rec["hbm_bytes_per_launch"] / w.min_bytes())
+    assert rec["kernel_trace"]["calls"] == 100
+    assert rec["kernel_trace"]["tflops_at_average"] == pytest.approx(
+        w.flops() / (avg_ns * 1e-9) / 1e12)
+    md = (out / "fa_fwd_ai2048_rocprof.md").read_text()
+    assert "2.200 GHz" in md and "rocprofv3 --pmc FETCH_SIZE" in md
+    assert json.loads((out / "fa_fwd_ai2048_hbm_counters.json").read_text())["sq"] == sq

@@ -66,6 +66,29 @@ def test_device_query_without_a_gpu(L, no_gpu):
     assert fa.fa_last_hip_error() == 0
 
 
+def test_device_info_without_a_gpu(L, no_gpu):
+    """Without a GPU the device query fails with FA_ERR_HIP and zeroed outputs; NULL
+    outputs are rejected before any HIP call."""
+    import ctypes
+    from concurrent.futures import ThreadPoolExecutor
+
+    def probe():
+        # on a thread of its own: the HIP error it records is per thread
+        cus, khz = ctypes.c_int(7), ctypes.c_int(7)
+        st = L.fa_device_info(0, ctypes.byref(cus), ctypes.byref(khz))
+        with pytest.raises(fa.FAError):
+            fa.fa_device_info(0)
+        return st, cus.value, khz.value, fa.fa_last_hip_error()
+
+    with ThreadPoolExecutor(1) as ex:
+        st, cus, khz, err = ex.submit(probe).result()
+    assert st == fa.FA_ERR_HIP and (cus, khz) == (0, 0) and err != 0
+    c = ctypes.c_int(0)
+    assert L.fa_device_info(0, None, ctypes.byref(c)) == fa.FA_ERR_NULL
+    assert L.fa_device_info(0, ctypes.byref(c), None) == fa.FA_ERR_NULL
+    assert fa.fa_last_hip_error() == 0
+
+
 def test_supported_query(L):
     for d in (1, 4, 63, 64, 65, 127, 128):
         for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16):

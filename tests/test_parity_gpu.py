@@ -371,6 +371,25 @@ def test_device_supported():
     assert fa.fa_device_supported(-1) == 0
 
 
+def test_device_info():
+    """CU count and peak engine clock agree with torch's device properties and with the
+    MI355X's published figures (256 CUs, 2.4 GHz); a missing device is an FA_ERR_HIP."""
+    dev = torch.cuda.current_device()
+    cus, khz = fa.fa_device_info(dev)
+    assert cus == torch.cuda.get_device_properties(dev).multi_processor_count
+    assert cus == 256
+    assert 1_500_000 <= khz <= 3_000_000
+    from concurrent.futures import ThreadPoolExecutor
+
+    def missing():  # on a thread of its own: the HIP error it records is per thread
+        with pytest.raises(fa.FAError) as e:
+            fa.fa_device_info(torch.cuda.device_count())
+        return e.value.status
+
+    with ThreadPoolExecutor(1) as ex:
+        assert ex.submit(missing).result() == fa.FA_ERR_HIP
+
+
 def test_raw_abi_call_matches_forward():
     w = workloads.get("tiny")
     q, k, v = (t.to(DEV) for t in workloads.make_inputs(w))
