@@ -8,8 +8,8 @@
  *  [P2] iq-universe.github.io, "FlashAttention은 어떻게 O(N²) 메모리 벽을 넘었나"
  *  [P3] ariser.io, "FlashAttention: 어텐션을 빠르게 만든 건 계산량보다 데이터
  *       이동이었다"
- *  [P2'] iq-universe.github.io, "FlashAttention: SRAM tiling으로 O(N²) HBM을
- *       우회하다" (the chapter's second page)
+ * [P2] sections are cited by their heading, e.g. [P2] "FlashAttention: SRAM tiling으로
+ * O(N²) HBM을 우회하다".
  *
  * The library never allocates device memory, keeps no pointer after a call returns
  * and needs no workspace except where an entry point takes one from the caller (the O(N)
@@ -17,9 +17,8 @@
  * exception, fa_fwd_splitkv_static, uses a fixed device array of its own. Its only
  * other global state is the compute-unit count and the LDS size per compute unit of each
  * device, read once per device (std::call_once) and immutable afterwards; they only
- * steer which of the call's own Q and K rows a workgroup pre-loads into the L2 and how
- * many 8-bit workgroups share a compute unit (performance hints, never correctness
- * inputs). Calls are reentrant and thread-safe (fa_fwd_splitkv_static: see its
+ * steer how many 8-bit workgroups share a compute unit (a performance hint, never a
+ * correctness input). Calls are reentrant and thread-safe (fa_fwd_splitkv_static: see its
  * comment). No C++ exception crosses this boundary.
  */
 #ifndef FA_H_
@@ -258,8 +257,9 @@ size_t fa_fwd_fa1_workspace_size(int B, int H, int N, int d);
  *   dQ = scale * dS K,   dK = scale * dS^T Q.
  *
  * P is not stored by the forward pass: it is recomputed block by block as
- * P_ij = exp(S_ij - lse_i) ([P1] FA2 section, the LSE identity; [P2'] the
- * paragraph on activation memory; [P3] "계산을 다시 하는 편이 싸다는 역설", which
+ * P_ij = exp(S_ij - lse_i) ([P1] FA2 section, the LSE identity; [P2] "FlashAttention:
+ * SRAM tiling으로 O(N²) HBM을 우회하다", the paragraph on recomputation in the backward
+ * pass; [P3] "계산을 다시 하는 편이 싸다는 역설", which
  * trades that recomputation for the N x N matrix's HBM traffic). D_i equals
  * rowsum(P * dP) (the softmax Jacobian), computed from dO and O.
  *

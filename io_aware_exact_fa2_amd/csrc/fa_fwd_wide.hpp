@@ -120,7 +120,9 @@ __device__ __forceinline__ float keep_if_le(float x, int c, int t) {
 // The softmax of one key tile, as a stream of VALU instructions ("ops") placed into the
 // MFMA slots of an iteration. A lane holds NPAIR pairs of scores per tile; per pair, ops
 // 0-1 are the two exponent arguments s c - m (FMA), 2-3 their exponentials, 4-5 the two
-// adds into the tile sums, 6 the 16-bit pack into the P operand. The three stages of
+// adds into the tile sums, 6 the 16-bit pack into the P operand. A query block's tile
+// sums start as the sums of its first two pairs (op 4 adds the pair, op 5 is dropped), so
+// no pair's probability is merely copied into a sum. The three stages of
 // consecutive pairs are staggered (step k holds the arguments of pair k, the
 // exponentials of pair k - LB and the sums and pack of pair k - LC), so an op never
 // reads the result of the op just before it. The ops go into the slots in stream order
@@ -129,8 +131,13 @@ __device__ __forceinline__ float keep_if_le(float x, int c, int t) {
 template <int NPAIR, int NSLOT>
 struct OpSched {
   int code[7 * NPAIR];  // 8 * pair + op
+  int n;                // ops in the stream
   int first[NSLOT + 1]; // ops [first[s], first[s + 1]) go into slot s
 };
+// Pairs 0, 1 (query block 0) and 4, 5 (query block 1) start the two tile sums of their
+// query block: pair v's scores sit in registers 8 (v / 8) + 2 (v % 4) of query block
+// (v / 4) % 2.
+constexpr bool sum_starter(int v) { return v < 8 && v % 4 < 2; }
 template <int NPAIR, int NSLOT, int LB, int LC, int SC_N, int NQK, int NPV, int PF, int NDMA>
 constexpr OpSched<NPAIR, NSLOT> make_op_sched() {
   OpSched<NPAIR, NSLOT> t{};
@@ -141,8 +148,10 @@ constexpr OpSched<NPAIR, NSLOT> make_op_sched() {
     for (int st = 0; st < 3; ++st) {
       const int v = k - lag[st];
       if (v < 0 || v >= NPAIR) continue;
-      for (int q = 0; q < 4 && ops_of[st][q] >= 0; ++q) t.code[n++] = 8 * v + ops_of[st][q];
+      for (int q = 0; q < 4 && ops_of[st][q] >= 0; ++q)
+        if (!(ops_of[st][q] == 5 && sum_starter(v))) t.code[n++] = 8 * v + ops_of[st][q];
     }
+  t.n = n;
   // issue costs in half-cycles
   const int op_cost[7] = {11, 11, 24, 24, 11, 11, 11};
   int fixed[NSLOT] = {};
@@ -162,7 +171,7 @@ constexpr OpSched<NPAIR, NSLOT> make_op_sched() {
     fixed[sl] = f;
     total += f;
   }
-  for (int i = 0; i < 7 * NPAIR; ++i) total += op_cost[t.code[i] % 8];
+  for (int i = 0; i < n; ++i) total += op_cost[t.code[i] % 8];
   long cum = 0;
   int o = 0;
   for (int sl = 0; sl < NSLOT; ++sl) {
@@ -170,7 +179,7 @@ constexpr OpSched<NPAIR, NSLOT> make_op_sched() {
     cum += fixed[sl];
     const long target = total * (sl + 1) / NSLOT;
     // take ops while that brings the running issue time closer to the target
-    while (o < 7 * NPAIR) {
+    while (o < n) {
       const int c = op_cost[t.code[o] % 8];
       if (cum + c <= target || (cum + c - target) < (target - cum)) {
         cum += c;
@@ -180,7 +189,7 @@ constexpr OpSched<NPAIR, NSLOT> make_op_sched() {
       }
     }
   }
-  t.first[NSLOT] = 7 * NPAIR;
+  t.first[NSLOT] = n;
   return t;
 }
 template <int NPAIR, int NSLOT, int LB, int LC, int SC_N, int NQK, int NPV, int PF, int NDMA>
@@ -348,6 +357,21 @@ fa_fwd_wide_kernel(const Params p) {
     }
   };
 
+  // S^T of tile t with its K rows read from global memory (the tile's ring slot may
+  // already hold a later tile): same operands, same accumulation order as qk_plain, so
+  // the same bits. Rows past N read row N - 1; the mask clears them.
+  auto qk_global = [&](int t, STile& s) {
+    zero(s);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      const int kb = i % (BC / 32), ds = i / (BC / 32);
+      const int row = min(t * BC + kb * 32 + key_of_row(l32), N - 1);
+      const u32x4_t kf = ld16(kg + (size_t)row * D + ds * 16 + hh * 8);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][ds], s[kb][qb]);
+    }
+  };
+
   // -inf on keys past N and, under the causal mask, on keys after the query; only tiles
   // that reach past N or cross the diagonal need it
   auto mask = [&](STile& s, int j) __attribute__((always_inline)) {
@@ -395,11 +419,11 @@ fa_fwd_wide_kernel(const Params p) {
       pq[bp][op - 2] = __builtin_amdgcn_exp2f(tq[bt][op - 2]);
       asm volatile("" : "+v"(pq[bp][op - 2]));
     } else if (op < 6) {
-      if (v == 0 || v == 4)  // first pair of its query block in the tile
-        ts[qb][op - 4] = pq[bp][op - 4];
+      if (sum_starter(v))  // op 4 only: sum v % 2 of the query block starts as the pair's
+        ts[qb][v % 2] = pq[bp][0] + pq[bp][1];
       else
         ts[qb][op - 4] += pq[bp][op - 4];
-      asm volatile("" : "+v"(ts[qb][op - 4]));
+      asm volatile("" : "+v"(ts[qb][sum_starter(v) ? v % 2 : op - 4]));
     } else {
       uint32_t w = E::pack(pq[bp][0], pq[bp][1]);
       asm volatile("" : "+v"(w));
@@ -408,7 +432,7 @@ fa_fwd_wide_kernel(const Params p) {
   };
   auto softmax_all = [&](const STile& s, PTile& pt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int o = 0; o < 7 * NPAIR; ++o) exp_op(s, pt, o);
+    for (int o = 0; o < FA_W_OPS.n; ++o) exp_op(s, pt, o);
   };
 
   // O~ in AGPRs is written by inline-assembly MFMAs the compiler does not track: pad
@@ -448,22 +472,26 @@ fa_fwd_wide_kernel(const Params p) {
       }
     return xhalf_max(__builtin_fmaxf(m0, m1)) * c;
   };
-  // The tile in the softmax stage may hold a probability above 2^tau (some lane's tile
-  // sum exceeds it): take its row max, raise the references that the rule raises, and
-  // recompute the tile's softmax against them.
-  auto fix_tile = [&](const STile& s, PTile& pt) __attribute__((always_inline)) {
+  // Tile t in the softmax stage may hold a probability above 2^tau (some lane's tile
+  // sum exceeds it): recompute its scores (the softmax stage has consumed the S^T tile
+  // by now, so it need not stay in registers for this rare case), take their row max,
+  // raise the references that the rule raises, and recompute the tile's softmax.
+  auto fix_tile = [&](int t, PTile& pt) {
+    STile sx;
+    qk_global(t, sx);
+    mask(sx, t);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float mx = row_max(s, qb);
+      const float mx = row_max(sx, qb);
       grow_max(qb, mx, __builtin_amdgcn_ballot_w64(mx > ms[qb] + p.tau));
     }
-    softmax_all(s, pt);
+    softmax_all(sx, pt);
   };
-  // Tile sums checked: all at most 2^tau, or the tile is fixed. Then they join l.
-  auto settle = [&](const STile& s, PTile& pt) __attribute__((always_inline)) {
+  // Tile sums checked: all at most 2^tau, or tile t is fixed. Then they join l.
+  auto settle = [&](int t, PTile& pt) __attribute__((always_inline)) {
     const float big = __builtin_fmaxf(__builtin_fmaxf(ts[0][0], ts[0][1]),
                                       __builtin_fmaxf(ts[1][0], ts[1][1]));
-    if (__builtin_amdgcn_ballot_w64(!(big <= thr)) != 0) fix_tile(s, pt);
+    if (__builtin_amdgcn_ballot_w64(!(big <= thr)) != 0) fix_tile(t, pt);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       ls[qb][0] += ts[qb][0];
@@ -583,7 +611,8 @@ fa_fwd_wide_kernel(const Params p) {
       __builtin_amdgcn_sched_barrier(0);
       if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(1, i + FA_W_PF);
 #pragma unroll
-      for (int o = 7 * NPAIR * sl / SB_N; o < 7 * NPAIR * (sl + 1) / SB_N; ++o) exp_op(sa, pa, o);
+      for (int o = FA_W_OPS.n * sl / SB_N; o < FA_W_OPS.n * (sl + 1) / SB_N; ++o)
+        exp_op(sa, pa, o);
       __builtin_amdgcn_sched_barrier(0);
     }
     mask(sb, 1);
@@ -622,7 +651,7 @@ fa_fwd_wide_kernel(const Params p) {
       PTile& p_mid = (u % 2 == 0) ? pb : pa;  // tile j+1
       if (wave_live && j < w_kt) {
         iteration(u, j, s_new, s_mid, p_mid, p_cur);
-        if (j + 1 < w_kt) settle(s_mid, p_mid);
+        if (j + 1 < w_kt) settle(j + 1, p_mid);
       } else {
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) copy_step(j + R + 1, (u + 1) % R, j + R - 1, (u + R - 1) % R, i);
