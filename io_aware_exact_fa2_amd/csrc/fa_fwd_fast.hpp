@@ -57,7 +57,7 @@
 
 // Interleave patterns (instructions per pipeline step) given to the machine scheduler.
 #ifndef FA_SG_B_VALU
-#define FA_SG_B_VALU 7    // VALU per S^T MFMA step (exponentials of the previous tile)
+#define FA_SG_B_VALU 6    // VALU per S^T MFMA step (exponentials of the previous tile)
 #endif
 #ifndef FA_SG_C_VALU
 #define FA_SG_C_VALU 2    // VALU per P V MFMA step (row max of the next tile)
@@ -316,9 +316,17 @@ fa_fwd_fast_kernel(const Params p) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e / 16][e % 16], c, -msc));
         const float p1 =
             __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e / 16][(e + 1) % 16], c, -msc));
-        lsum0 += p0;
-        lsum1 += p1;
-        pb[e / 8][(e % 8) / 2] = E::pack(p0, p1);
+        const uint32_t w = E::pack(p0, p1);
+        pb[e / 8][(e % 8) / 2] = w;
+        if constexpr (BF16) {
+          lsum0 += p0;
+          lsum1 += p1;
+        } else {
+          // half-precision P: l sums the rounded pair (one dot2), each term within 2^-11
+          // of its probability, so L moves by at most that relative amount
+          float& acc = (e / 2) % 2 ? lsum1 : lsum0;
+          acc = E::sum2(w, acc);
+        }
       }
       copy_step(cp, i);
     }
