@@ -254,17 +254,24 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(const BwdParams p) {
       // k0 + 32 kb + 8 hh + rc(r), allowed when rc(r) <= t
       const int t = lim - (k0 + 32 * kb + 8 * hh);
       u32x4_t dsop[2];
+      auto body = [&](bool masked) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float v2[2];
+        for (int r = 0; r < 16; r += 2) {
+          float v2[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int rc = key_of_reg(r + e, 0);
-          const float pr = rc <= t ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + e], p.c, -L2)) : 0.f;
-          v2[e] = pr * (dpt[r + e] - Dq);
+          for (int e = 0; e < 2; ++e) {
+            const int rc = key_of_reg(r + e, 0);
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r + e], p.c, -L2));
+            if (masked && !(rc <= t)) pr = 0.f;
+            v2[e] = pr * (dpt[r + e] - Dq);
+          }
+          dsop[r / 8][(r % 8) / 2] = E::pack(v2[0], v2[1]);
         }
-        dsop[r / 8][(r % 8) / 2] = E::pack(v2[0], v2[1]);
-      }
+      };
+      // a register's key offset within its half is at most 23: when every lane allows
+      // that much (tiles below the diagonal, away from the ragged end), no score is masked
+      if (__builtin_amdgcn_ballot_w64(!(t >= 23)) == 0) body(false);
+      else body(true);
       // dQ^T += K^T dS^T over these 32 keys (two 16-key steps)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)

@@ -80,6 +80,19 @@ template <> struct Elt<false> {
   }
 };
 
+// acc += A B with the accumulator held in AGPRs, for accumulators that only MFMAs touch
+// until the end (the ones the VALU reads stay in VGPRs). Written out because the
+// compiler picks one register file for all MFMA accumulators of a kernel. The compiler
+// does not see these as matrix instructions: callers keep the sources of one step live
+// until the next step is issued, and pad before the VALU reads the accumulator.
+template <bool BF16>
+__device__ __forceinline__ void mfma_acc_agpr(f32x16_t& acc, u32x4_t a, u32x4_t b) {
+  if (BF16)
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;

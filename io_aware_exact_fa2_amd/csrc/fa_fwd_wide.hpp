@@ -68,17 +68,6 @@ struct WideGeom {
   static_assert(R >= 4 && R % 2 == 0, "the ring holds the tiles of three stages");
 };
 
-// O~ += A B with the accumulator held in AGPRs (the S^T accumulators stay in VGPRs,
-// where the VALU reads them). Written out because the compiler picks one register
-// file for all MFMA accumulators of a kernel.
-template <bool BF16>
-__device__ __forceinline__ void mfma_acc_agpr(f32x16_t& acc, u32x4_t a, u32x4_t b) {
-  if (BF16)
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
 // Raw buffer resource over `bytes` bytes at address a (stride 0, 32-bit format): reads
 // past the end return zeros.
 __device__ __forceinline__ u32x4_t buffer_rsrc(uint64_t a, uint32_t bytes) {
