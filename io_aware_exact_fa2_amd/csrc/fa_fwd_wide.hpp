@@ -74,12 +74,12 @@ __device__ __forceinline__ u32x4_t buffer_rsrc(uint64_t a, uint32_t bytes) {
   return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
 }
 
-// The copies and the Q loads are issued as inline assembly, so the compiler's memory
-// counter model does not see them and adds no waits of its own: the kernel orders
-// them with explicit vmcnt waits and its ring barrier. One 16-byte-per-lane HBM -> LDS
-// copy: lane l's 16 bytes at byte offset voff of the buffer land at LDS address
-// lds + lds_off + 16 l (M0 holds the wave's LDS base); bytes past the buffer's size
-// read as 0.
+// The HBM -> LDS copies (K, V and the Q rows) are issued as inline assembly, so the
+// compiler's memory counter model does not see them and adds no waits of its own: the
+// kernel orders them with explicit vmcnt waits and its ring barrier. They write no
+// register. One 16-byte-per-lane copy: lane l's 16 bytes at byte offset voff of the
+// buffer land at LDS address lds + lds_off + 16 l (M0 holds the wave's LDS base); bytes
+// past the buffer's size read as 0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(u32x4_t rsrc, uint32_t voff, uint32_t lds,
@@ -88,13 +88,6 @@ __device__ __forceinline__ void lds_copy16(u32x4_t rsrc, uint32_t voff, uint32_t
                :: "v"(voff), "s"(rsrc), "s"(lds), "n"(lds_off) : "m0", "scc");
 }
 #pragma clang diagnostic pop
-// 16-byte global load; the result may only be read after an explicit vmcnt wait
-// that covers it.
-__device__ __forceinline__ u32x4_t global_load16(const uint16_t* p) {
-  u32x4_t x;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(x) : "v"(p));
-  return x;
-}
 
 // x = (c <= t) ? x : -inf, with c a constant after unrolling. Compare and select
 // stay one pair, so no lane masks pile up in scalar registers across a tile.
@@ -224,7 +217,9 @@ fa_fwd_wide_kernel(const Params p) {
   const int w_last_q = min(qbase[1] + 32, N) - 1;
   const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
 
-  // ---- HBM -> LDS copies (see the two-stage kernel for the layout) ------------------
+  // ---- HBM -> LDS copies: lane l of a wave's copy i of a tile writes 16-byte chunk
+  // position (NW i + wid) * 64 + l of the tile (row-major, CPR chunks per row) and
+  // fetches the row's logical chunk that the swizzle puts there ---------------------
   constexpr uint32_t II_BYTES = NW * 64 * 16;
   static_assert((NW * 64 / CPR) % 16 == 0, "copies are whole 16-row groups");
   uint32_t koff, voff;
@@ -261,23 +256,35 @@ fa_fwd_wide_kernel(const Params p) {
   };
 
   // ---- Q fragments (B operands of S^T = K Q^T), in AGPRs for the whole loop ----------
+  // The wave's 64 Q rows (query block 0, then 1; rows past N repeat row N - 1, never
+  // stored) go HBM -> LDS like the K tiles, in whole 1 KB copies, into the wave's slot of
+  // the V ring (idle until V_0 is copied, after the prologue's first barrier): copy i,
+  // lane l moves chunk position (64 i + l) % CPR of wave row (64 i + l) / CPR, which
+  // holds the row's logical chunk position ^ swz_k(row), as in a K tile. Then the wave
+  // reads its fragments from there, conflict-free as the K operand reads.
+  // Prologue copies after the Q rows: K_0 .. K_3; V_0 .. V_2 follow the first barrier,
+  // K_4 the second one (once every wave is done with K_0's slot).
   u32x4_t qf[2][D / 16];
+  const uint32_t q_lds =  // slot wid of the V ring
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(vbuf + wid * CHUNKS));
+  {
+    static_assert(64 * CPR == CHUNKS, "a wave's Q rows fill one ring slot");
+    const u32x4_t rq = buffer_rsrc((uint64_t)(uintptr_t)qg, (uint32_t)N * D * 2);
+    // (an opaque copy of the lane index keeps these row numbers from being shared with
+    // the epilogue's, which would hold them in registers across the whole loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = min(qbase[qb] + l32, N - 1);
-#pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds)
-      qf[qb][ds] = global_load16(qg + (size_t)qi * D + ds * 16 + hh * 8);
+    for (int i = 0; i < CPR; ++i) {
+      const int f = 64 * i + ln, r = f / CPR, ph = f % CPR;
+      const int qi = min(qbase[r / 32] + (r % 32), N - 1);
+      lds_copy16(rq, (uint32_t)(qi * D + (ph ^ swz_k<D>(r)) * 8) * 2u, q_lds, i * 1024);
+    }
   }
-  // prologue copies, in this order: K_0, K_1, V_0, K_2, V_1, K_3, V_2 (K_4 follows once
-  // every wave is done with K_0's slot)
   copy_k(0);
   copy_k(1);
-  copy_v(0);
   copy_k(2);
-  copy_v(1);
   copy_k(3);
-  copy_v(2);
 
   // ---- running state ---------------------------------------------------------------
   f32x16_t oacc[D / 32][2];
@@ -293,7 +300,9 @@ fa_fwd_wide_kernel(const Params p) {
   const float c = p.c;
   const float thr = __builtin_amdgcn_exp2f(p.tau);  // largest probability allowed
 
-  // ---- per-lane LDS read addresses (see the two-stage kernel) ------------------------
+  // ---- per-lane LDS read addresses: lane l reads K tile row key_of_row(l % 32), chunk
+  // 2 ds + l / 32 (the ds step folds in by XOR), and V^T transposed, 4 rows x 4 chunks
+  // per 16-lane group ---------------------------------------------------------------
   uint32_t kaddr0;
   {
     const int row = key_of_row(l32);
@@ -572,17 +581,25 @@ fa_fwd_wide_kernel(const Params p) {
   // ---- prologue: S^T and softmax of tile 0, S^T of tile 1 -----------------------------
   STile sa, sb;
   PTile pa, pb;
-  // Q, K_0 and K_1 have landed (the 5 copy groups issued after K_1 may be in flight)
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * PW) : "memory");
+  // Q, K_0 and K_1 have landed (K_2 and K_3 may be in flight)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PW) : "memory");
+  {
+    // wave row 32 qb + l32, logical chunk 2 ds + hh (16 columns ds, half hh)
+    const uint32_t qaddr = (uint32_t)(uintptr_t)vbuf + (uint32_t)(wid * CHUNKS * 16) +
+                           (uint32_t)((l32 * CPR + (hh ^ swz_k<D>(l32))) * 16);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      asm volatile("" : "+v"(qf[qb][ds]));
-      qf[qb][ds] ^= p.qsign;
-      asm volatile("" : "+a"(qf[qb][ds]));
-    }
-  ring_barrier();
+      for (int ds = 0; ds < D / 16; ++ds) {
+        qf[qb][ds] = *(lds_u32x4_t*)(uintptr_t)((qaddr ^ (uint32_t)(ds << 5)) + qb * 32 * CPR * 16);
+        qf[qb][ds] ^= p.qsign;
+        asm volatile("" : "+a"(qf[qb][ds]));
+      }
+  }
+  ring_barrier();  // every wave has its Q fragments: the V ring is free for V_0 .. V_2
+  copy_v(0);
+  copy_v(1);
+  copy_v(2);
   if (wave_live) {
     qk_plain(0, sa);
     mask(sa, 0);
