@@ -150,6 +150,24 @@ def test_reduced_shapes(case):
     _full_case(w)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+@pytest.mark.parametrize("scale_sign", [1.0, -1.0])
+def test_several_items_per_workgroup(dt, scale_sign):
+    """A grid several times the CU count at d = 128 without the causal mask: 600 heads of
+    N = 300 give 1200 workgroups of 256 queries, and every head's second one has waves
+    wholly past N; both signs of the scale."""
+    w = Workload(f"items_{dt}", 2, 300, 300, 128, dt, False, seed=5100 + (dt == "fp16"))
+    _full_case(w, scale=scale_sign * w.scale,
+               name=f"items/{dt}/2x300x300x128/scale{'-' if scale_sign < 0 else '+'}")
+
+
+def test_several_items_lazy_rescale_off():
+    """The same grid with the literal per-block update on spiked inputs: tiles are fixed
+    often, their scores recomputed from the K rows of the workgroup's own head."""
+    w = Workload("items_tau0", 1, 600, 300, 128, "bf16", False, seed=5103, dist="stress")
+    _full_case(w, rescale_log2=0.0, name="items/tau0/1x600x300x128/stress")
+
+
 @pytest.mark.parametrize("d", [1, 2, 8, 16, 33, 48, 63, 65, 96, 100, 127])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_head_dims(d, causal):
