@@ -229,11 +229,12 @@ fa_fwd_wide_kernel(const Params p) {
     voff = (uint32_t)(row * D + (ph ^ swz_v<D>(row)) * 8) * 2u;
   }
   // the buffer of tile t spans its rows below N (the range check zero-fills the rest);
-  // tiles past the last are clamped to it
+  // a tile past the last (the pipeline's drain reads it and drops the results) has an
+  // empty buffer, so its copies write zeros and read no memory
   auto tile_rsrc = [&](const uint16_t* src, int t) {
     const int k0 = min(t, n_kt - 1) * BC;
     return buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)k0 * D),
-                       (uint32_t)(min(N - k0, BC) * D * 2));
+                       t < n_kt ? (uint32_t)(min(N - k0, BC) * D * 2) : 0u);
   };
   const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(kbuf + wid * 64));
   const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(vbuf + wid * 64));
