@@ -418,6 +418,175 @@ def summarize_profile(workload, dirs, copy_mib, path="fwd", cmd_args="", out_dir
     return hbm
 
 
+def _all_kernel_stats(directory, pred):
+    """(name, calls, average ns, min ns, max ns) of every kernel that pred accepts."""
+    out = []
+    for r in _csv_rows(directory, "kernel_stats.csv"):
+        if pred(r["Name"]):
+            out.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                        float(r["MaxNs"])))
+    return sorted(out)
+
+
+def _counters_by_kernel(directory, pred):
+    acc = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if pred(r["Kernel_Name"]):
+            acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def _shape(w, path="fwd"):
+    mask = "causal" if w.causal else "non-causal"
+    dt = "E4M3 Q, K, V with per-tensor scales, bf16 O" if path == "fp8" else w.dtype
+    return f"B={w.B}, H={w.H}, N={w.N}, d={w.d}, {dt}, {mask}"
+
+
+def summarize_traces(path, entries, sq_dirs=None, hbm_dirs=None, copy_mib=512,
+                     cmd_args=" --steps 20 --warmup 3", out_dir=None):
+    """profiles/fa_<path>_rocprof.md (and a JSON of its figures) from rocprofv3 runs of
+    `bench.py --path <path>` (bwd: the three backward kernels; fp8: the 8-bit forward;
+    fa1: the FA1-order forward): a --kernel-trace --stats directory per workload, for the
+    backward also the two SQ --pmc passes of its first workload, for fa1 also the
+    FETCH_SIZE / WRITE_SIZE runs."""
+    import workloads
+
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    pred = {"bwd": lambda n: "fa_bwd" in n, "fp8": lambda n: "fa_fwd_fp8" in n,
+            "fa1": lambda n: "fa_fwd_fa1" in n}[path]
+    factor = 2.5 if path == "bwd" else 1.0
+    title = {"bwd": "fa_bwd backward kernels", "fp8": "fa_fwd_fp8 (E4M3 forward)",
+             "fa1": "fa_fwd_fa1 (the FA1 loop order)"}[path]
+    rec = {"path": path, "kernel_source_sha256_16": kernel_hash(), "workloads": {}}
+    lines = [f"# {title} — rocprofv3 summary", "",
+             f"Kernel source hash (bench.py `kernel_hash`): {rec['kernel_source_sha256_16']}. "
+             "Seeded synthetic inputs from `workloads`; all commands run from the repository "
+             "root, output directories are placeholders; every figure below is computed from "
+             "the runs by the summary command.", "", "## Kernel trace (`--kernel-trace --stats`)",
+             ""]
+    for wl, kt_dir in entries:
+        lines.append(f"    rocprofv3 --kernel-trace --stats -f csv -d <kt_dir_{wl}> -o kt -- "
+                     f"python -u bench.py --workload {wl} --path {path}{cmd_args}")
+    lines.append("")
+    if path == "bwd":
+        lines += ["Work convention: 2.5x the forward flops (five N x N x d products), halved "
+                  "for causal; one backward is the three kernels once each.", "",
+                  "| workload | shape | kernel | calls | average µs | min µs | max µs |",
+                  "|---|---|---|---|---|---|---|"]
+    else:
+        lines += ["| workload | shape | kernel | calls | average µs | min µs | max µs | TFLOPS |",
+                  "|---|---|---|---|---|---|---|---|"]
+    summary = []
+    for wl, kt_dir in entries:
+        w = workloads.get(wl)
+        ks = _all_kernel_stats(kt_dir, pred)
+        total = sum(k[2] for k in ks)
+        tf = factor * w.flops() / (total * 1e-9) / 1e12 if total else 0.0
+        rec["workloads"][wl] = {"kernels": {k[0]: {"calls": k[1], "average_ns": k[2],
+                                                   "min_ns": k[3], "max_ns": k[4]} for k in ks},
+                                "sum_of_averages_ns": total, "tflops": tf}
+        for k in ks:
+            row = f"| {wl} | {_shape(w, path)} | `{k[0]}` | {k[1]} | {k[2] / 1e3:.1f} | " \
+                  f"{k[3] / 1e3:.1f} | {k[4] / 1e3:.1f} |"
+            if path != "bwd":
+                row += f" {w.flops() / (k[2] * 1e-9) / 1e12:.1f} |"
+            lines.append(row)
+        summary.append((wl, total, tf))
+    lines.append("")
+    if path == "bwd":
+        lines += ["| workload | backward µs (sum of the averages) | TFLOPS (2.5x convention) | "
+                  "% of 2500 |", "|---|---|---|---|"]
+        lines += [f"| {wl} | {t / 1e3:.1f} | {tf:.1f} | {100 * tf / 2500:.1f} |"
+                  for wl, t, tf in summary]
+        lines.append("")
+    elif path == "fp8":
+        lines += ["Against the 5000 TFLOPS dense FP8 peak: " + ", ".join(
+            f"{wl} {100 * tf / 5000:.1f}%" for wl, _, tf in summary) + ".", ""]
+    if sq_dirs:
+        wl0 = entries[0][0]
+        c1 = _counters_by_kernel(sq_dirs[0], pred)
+        c2 = _counters_by_kernel(sq_dirs[1], pred)
+        lines += [f"## SQ counters, {wl0} (two `--pmc` passes, mean per dispatch of each kernel)",
+                  "", f"    rocprofv3 --pmc {SQ_PASS1} -f csv -d <sq1_dir> -o p -- python -u "
+                  f"bench.py --workload {wl0} --path {path}{cmd_args}",
+                  "", f"    rocprofv3 --pmc {SQ_PASS2} -f csv -d <sq2_dir> -o p -- python -u "
+                  f"bench.py --workload {wl0} --path {path}{cmd_args}", "",
+                  "| kernel | VALU per MFMA | MFMA busy % of active cycles | clock GHz | issuing % "
+                  "of wave cycles | s_waitcnt % | waiting to issue % | LDS bank-conflict cycles |",
+                  "|---|---|---|---|---|---|---|---|"]
+        kt = dict((k[0], k[2]) for k in _all_kernel_stats(entries[0][1], pred))
+        rec["sq"] = {}
+        for name in sorted(c1):
+            a, b = c1[name], c2.get(name, {})
+            if not a.get("SQ_INSTS_MFMA") or name not in kt:
+                continue
+            act = a["GRBM_GUI_ACTIVE"] / N_XCD
+            sq = {"valu_insts_per_mfma": a["SQ_INSTS_VALU"] / a["SQ_INSTS_MFMA"],
+                  "mfma_busy_pct": 100 * a["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / act,
+                  "clock_GHz_under_load": act / (kt[name] * 1e-9) / 1e9,
+                  "lds_bank_conflict_cycles": a["SQ_LDS_BANK_CONFLICT"]}
+            if b.get("SQ_WAVE_CYCLES"):
+                sq["issue_pct_of_wave_cycles"] = 100 * b["SQ_ACTIVE_INST_ANY"] / b["SQ_WAVE_CYCLES"]
+                sq["waitcnt_pct_of_wave_cycles"] = 100 * b["SQ_WAIT_ANY"] / b["SQ_WAVE_CYCLES"]
+                sq["wait_issue_pct_of_wave_cycles"] = 100 * b["SQ_WAIT_INST_ANY"] / b["SQ_WAVE_CYCLES"]
+            rec["sq"][name] = {**sq, "counters": {**a, **b}}
+            lines.append(f"| `{name}` | {sq['valu_insts_per_mfma']:.2f} | {sq['mfma_busy_pct']:.1f} | "
+                         f"{sq['clock_GHz_under_load']:.3f} | {sq.get('issue_pct_of_wave_cycles', 0):.1f} | "
+                         f"{sq.get('waitcnt_pct_of_wave_cycles', 0):.1f} | "
+                         f"{sq.get('wait_issue_pct_of_wave_cycles', 0):.1f} | "
+                         f"{sq['lds_bank_conflict_cycles']:.6g} |")
+        lines += ["", "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 "
+                  "XCDs); the clock is GRBM_GUI_ACTIVE / 8 / the kernel's trace average; the "
+                  "issue and wait shares divide by SQ_WAVE_CYCLES.", ""]
+    if hbm_dirs:
+        wl0 = entries[0][0]
+        hrec = summarize_hbm(wl0, hbm_dirs[0], hbm_dirs[1], copy_mib,
+                             os.path.join(out_dir, f"fa_{path}_{wl0}_hbm_counters.json"),
+                             "see the summary", path)
+        rec["hbm"] = {k: hrec[k] for k in ("hbm_bytes_per_launch", "fetch_bytes_per_launch",
+                                           "write_bytes_per_launch", "fetch_scale",
+                                           "write_scale")}
+        m = hrec["io_model"]
+        lines += ["## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`)", "",
+                  f"    rocprofv3 --pmc FETCH_SIZE -f csv -d <fetch_dir> -o p -- python -u bench.py "
+                  f"--workload {wl0} --path {path}{cmd_args} --calibrate-copy-mib {copy_mib}", "",
+                  f"    rocprofv3 --pmc WRITE_SIZE -f csv -d <write_dir> -o p -- python -u bench.py "
+                  f"--workload {wl0} --path {path}{cmd_args} --calibrate-copy-mib {copy_mib}", "",
+                  f"Counters scaled by a plain {copy_mib} MiB copy in the same run (FETCH_SIZE "
+                  f"scale {hrec['fetch_scale']:.3f}, WRITE_SIZE scale {hrec['write_scale']:.3f}).", "",
+                  "| | model (the pages' HBM column, this kernel's element sizes) | measured |",
+                  "|---|---|---|",
+                  f"| FA1 order (this kernel), fetch GB | {m['model_fetch_bytes'] / 1e9:.3f} | "
+                  f"{hrec['fetch_bytes_per_launch'] / 1e9:.3f} |",
+                  f"| FA1 order (this kernel), write GB | {m['model_write_bytes'] / 1e9:.3f} | "
+                  f"{hrec['write_bytes_per_launch'] / 1e9:.3f} |"]
+        fa2 = profile_record(wl0)
+        if fa2 is not None:
+            m2 = fa2["io_model"]
+            lines += [f"| FA2 order (fa_fwd, from `profiles/fa_fwd_{wl0}_hbm_counters.json`), "
+                      f"fetch GB | {m2['model_fetch_bytes'] / 1e9:.3f} | "
+                      f"{fa2['fetch_bytes_per_launch'] / 1e9:.3f} |",
+                      f"| FA2 order (fa_fwd), write GB | {m2['model_write_bytes'] / 1e9:.3f} | "
+                      f"{fa2['write_bytes_per_launch'] / 1e9:.3f} |"]
+        lines += ["", "Model: the HBM column of the FA1/FA2 comparison table of "
+                  "currybab.bearblog.dev (section \"정리\"): FA1 reads Q T_c times and reads "
+                  "and writes O_i T_c times; FA2 reads K and V T_r times, Q once and writes O "
+                  "once. The FA1 order meets its model to the byte (its re-read tensors do not "
+                  "fit an XCD's 4 MB L2); the FA2 order's K/V re-reads are served by the L2, "
+                  "since all query tiles of a head run at once on one XCD.", ""]
+    lines.append("    python bench.py --path " + path + " --summarize-traces " + " ".join(
+        f"{wl}=<kt_dir_{wl}>" for wl, _ in entries) +
+        (" --sq-dirs <sq1_dir> <sq2_dir>" if sq_dirs else "") +
+        (f" --hbm-dirs <fetch_dir> <write_dir> --calibrate-copy-mib {copy_mib}" if hbm_dirs else ""))
+    lines.append("")
+    with open(os.path.join(out_dir, f"fa_{path}_rocprof.md"), "w") as f:
+        f.write("\n".join(lines))
+    with open(os.path.join(out_dir, f"fa_{path}_counters.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def profile_record(workload: str, path: str = "fwd"):
     """The committed counter summary of a workload, if it was taken on the current
     kernel source; else None."""
@@ -517,10 +686,21 @@ def main(argv=None):
                     metavar=("KT_DIR", "SQ1_DIR", "SQ2_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/*_rocprof.md and *_hbm_counters.json from five "
                          "rocprofv3 runs (no GPU work)")
+    ap.add_argument("--summarize-traces", nargs="+", metavar="WORKLOAD=KT_DIR",
+                    help="with --path bwd|fp8|fa1: write profiles/fa_<path>_rocprof.md from "
+                         "kernel-trace runs (no GPU work)")
+    ap.add_argument("--sq-dirs", nargs=2, metavar=("SQ1_DIR", "SQ2_DIR"))
+    ap.add_argument("--hbm-dirs", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-args", default=" --cpu-budget 0 --also '' --backward '' "
                     "--fp8 '' --steps 20 --warmup 3",
                     help="bench.py arguments the profiled runs used (recorded)")
     a = ap.parse_args(argv)
+    if a.summarize_traces:
+        entries = [tuple(e.split("=", 1)) for e in a.summarize_traces]
+        rec = summarize_traces(a.path, entries, a.sq_dirs, a.hbm_dirs,
+                               a.calibrate_copy_mib or 512)
+        print(json.dumps({k: v["tflops"] for k, v in rec["workloads"].items()}))
+        return 0
     if a.summarize_profile:
         rec = summarize_profile(a.workload, a.summarize_profile, a.calibrate_copy_mib or 512,
                                 a.path, a.profile_args)

@@ -84,3 +84,40 @@ def test_profile_summary_arithmetic(tmp_path):
     md = (out / "fa_fwd_ai2048_rocprof.md").read_text()
     assert "2.200 GHz" in md and "rocprofv3 --pmc FETCH_SIZE" in md
     assert json.loads((out / "fa_fwd_ai2048_hbm_counters.json").read_text())["sq"] == sq
+
+
+def test_trace_summary_backward(tmp_path):
+    """The backward summary sums its three kernels' trace averages into one pass and
+    prices it at 2.5x the forward flops; the SQ table is per kernel."""
+    w = workloads.get("ai2048")
+    names = ["void fa::fa_bwd_delta_kernel<true, 128>(fa::BwdParams)",
+             "void fa::fa_bwd_dkdv_kernel<true, 128, false>(fa::BwdParams)",
+             "void fa::fa_bwd_dq_kernel<true, 128, false>(fa::BwdParams)"]
+    avgs = [10_000.0, 300_000.0, 200_000.0]
+    kt = str(tmp_path / "kt")
+    _write(os.path.join(kt, "host", "kt_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+            "StdDev"],
+           [[COPY, 1, 5, 5, 0, 5, 5, 0]] + [[n, 10, 10 * a, a, 30, a, a, 0]
+                                             for n, a in zip(names, avgs)])
+    sq1, sq2 = str(tmp_path / "sq1"), str(tmp_path / "sq2")
+    grbm = 8 * 2.0e9 * 300_000e-9
+    _pmc(sq1, {names[1]: {"GRBM_GUI_ACTIVE": [grbm], "SQ_INSTS_MFMA": [100.0],
+                          "SQ_INSTS_VALU": [650.0], "SQ_VALU_MFMA_BUSY_CYCLES":
+                          [0.25 * 1024 * grbm / 8], "SQ_LDS_BANK_CONFLICT": [0.0]}})
+    _pmc(sq2, {names[1]: {"SQ_WAVE_CYCLES": [10.0], "SQ_ACTIVE_INST_ANY": [4.0],
+                          "SQ_WAIT_ANY": [3.0], "SQ_WAIT_INST_ANY": [2.0]}})
+    out = tmp_path / "out"
+    out.mkdir()
+    rec = bench.summarize_traces("bwd", [("ai2048", kt)], (sq1, sq2), out_dir=str(out))
+    total = sum(avgs)
+    assert rec["workloads"]["ai2048"]["sum_of_averages_ns"] == pytest.approx(total)
+    assert rec["workloads"]["ai2048"]["tflops"] == pytest.approx(
+        2.5 * w.flops() / (total * 1e-9) / 1e12)
+    sq = rec["sq"][names[1]]
+    assert sq["valu_insts_per_mfma"] == pytest.approx(6.5)
+    assert sq["mfma_busy_pct"] == pytest.approx(25.0)
+    assert sq["clock_GHz_under_load"] == pytest.approx(2.0)
+    assert sq["waitcnt_pct_of_wave_cycles"] == pytest.approx(30.0)
+    md = (out / "fa_bwd_rocprof.md").read_text()
+    assert "--summarize-traces ai2048=<kt_dir_ai2048>" in md and names[2] in md
