@@ -331,9 +331,11 @@ fa_fwd_fast_kernel(const Params p) {
       copy_step(cp, i);
     }
     l_part += lsum0 + lsum1;
-    // keep the exponentials in this block (no sinking into the P V block)
+    // keep the exponentials in this block (no sinking into the P V block): a use of the
+    // packed operands here. (A tied in/out operand did the same but cost 8 register
+    // moves per tile to bring them back into the operand registers.)
 #pragma unroll
-    for (int st = 0; st < BC / 16; ++st) asm volatile("" : "+v"(pb[st]));
+    for (int st = 0; st < BC / 16; ++st) asm volatile("" ::"v"(pb[st]));
 #if FA_SG_ON
     __builtin_amdgcn_sched_group_barrier(0x100, FA_SG_PREFETCH, 0);
 #pragma unroll

@@ -41,7 +41,7 @@
 #include "fa_common.hpp"
 
 #ifndef FA_W_PF
-#define FA_W_PF 2  // MFMA steps an LDS operand read runs ahead
+#define FA_W_PF 3  // MFMA steps an LDS operand read runs ahead
 #endif
 
 namespace fa {
@@ -86,6 +86,20 @@ __device__ __forceinline__ void lds_copy16(u32x4_t rsrc, uint32_t voff, uint32_t
                                            int lds_off /* a constant after unrolling */) {
   asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voff), "s"(rsrc), "s"(lds), "n"(lds_off) : "m0", "scc");
+}
+// The main loop's copies keep M0 one copy ahead: each issues its load with the LDS
+// address the previous one left in M0, then sets M0 to the next copy's (saving the
+// set-up and the wait state in front of every load). An LDS copy needs one instruction
+// between the M0 write and itself; the loop's copies sit two MFMA slots apart, and
+// callers that issue them back to back put an s_nop in between. Nothing else writes M0
+// while the loop runs.
+__device__ __forceinline__ void lds_copy16_chained(u32x4_t rsrc, uint32_t voff, uint32_t next_lds,
+                                                   int next_off /* a constant after unrolling */) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_add_u32 m0, %2, %3"
+               :: "v"(voff), "s"(rsrc), "s"(next_lds), "n"(next_off) : "m0", "scc");
+}
+__device__ __forceinline__ void set_m0(uint32_t lds, int off /* a constant */) {
+  asm volatile("s_add_u32 m0, %0, %1" :: "s"(lds), "n"(off) : "m0", "scc");
 }
 #pragma clang diagnostic pop
 
@@ -216,6 +230,10 @@ fa_fwd_wide_kernel(const Params p) {
   const bool wave_live = wq0 < N;
   const int w_last_q = min(qbase[1] + 32, N) - 1;
   const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
+  // the first tile that reaches past N or, under the causal mask, past the wave's first
+  // query (key t BC + BC - 1 > wq0), and the number of the wave's tiles from there on
+  const int t_mask = CAUSAL ? min(N / BC, (wq0 + 1) / BC) : N / BC;
+  const uint32_t n_masked = (uint32_t)max(w_kt - t_mask, 0);
 
   // ---- HBM -> LDS copies: lane l of a wave's copy i of a tile writes 16-byte chunk
   // position (NW i + wid) * 64 + l of the tile (row-major, CPR chunks per row) and
@@ -254,6 +272,46 @@ fa_fwd_wide_kernel(const Params p) {
   auto copy_v = [&](int vt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = PW; i < NDMA; ++i) copy_step(0, 0, vt, vt % R, i);
+  };
+  // The loop's copies: iteration u of the group of R iterations that starts at tile j0
+  // copies K_{j0+u+R+1} into ring slot (u+1) % R and V_{j0+u+R-1} into slot (u+R-1) % R.
+  // Their buffers are taken relative to the group's base (tile j0's address kgj / vgj,
+  // and remj, the bytes of rows below the last tile's end from tile j0 on): a tile's
+  // buffer then reaches from its first row to that end, so rows past N, and tiles past
+  // the last, read as zeros as above. (The address's high word is used as it is: device
+  // addresses stay below 2^48, so it never reaches the resource's stride field.)
+  constexpr uint32_t TB = (uint32_t)CHUNKS * 16u;  // bytes of a K (or V) tile
+  const uint32_t kv_bytes = (uint32_t)min(n_kt * BC, N) * (uint32_t)(D * 2);
+  const uint16_t* kgj = kg;
+  const uint16_t* vgj = vg;
+  uint32_t remj = kv_bytes;
+  auto rsrc_rel = [&](const uint16_t* base, int dt) __attribute__((always_inline)) {
+    const uint64_t a = (uint64_t)(uintptr_t)base + (uint64_t)dt * TB;
+    // max(remj, o) - o on the scalar unit (the compiler would saturate on the VALU)
+    uint32_t size;
+    asm("s_max_u32 %0, %1, %2\n\ts_sub_u32 %0, %0, %2"
+        : "=&s"(size) : "s"(remj), "n"(dt * TB) : "scc");
+    return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32), size, (uint32_t)kBufferWord3};
+  };
+  // copy i of iteration u (K copies first); M0 holds its LDS address and is then set to
+  // the next copy's: copy i + 1, or copy 0 of iteration u + 1
+  auto copy_loop = [&](int u, int i) __attribute__((always_inline)) {
+    const int ks = (u + 1) % R, vs = (u + R - 1) % R;
+    if (i < PW) {
+      const u32x4_t rs = rsrc_rel(kgj, u + R + 1);
+      if (i + 1 < PW)
+        lds_copy16_chained(rs, koff + II_BYTES * i, k_lds, ks * CHUNKS * 16 + (i + 1) * NW * 1024);
+      else
+        lds_copy16_chained(rs, koff + II_BYTES * i, v_lds, vs * CHUNKS * 16);
+    } else if (i < NDMA) {
+      const u32x4_t rs = rsrc_rel(vgj, u + R - 1);
+      const int iv = i - PW;
+      if (i + 1 < NDMA)
+        lds_copy16_chained(rs, voff + II_BYTES * iv, v_lds,
+                           vs * CHUNKS * 16 + (iv + 1) * NW * 1024);
+      else
+        lds_copy16_chained(rs, voff + II_BYTES * iv, k_lds, ((u + 2) % R) * CHUNKS * 16);
+    }
   };
 
   // ---- Q fragments (B operands of S^T = K Q^T), in AGPRs for the whole loop ----------
@@ -374,10 +432,9 @@ fa_fwd_wide_kernel(const Params p) {
   // -inf on keys past N and, under the causal mask, on keys after the query; only tiles
   // that reach past N or cross the diagonal need it
   auto mask = [&](STile& s, int j) __attribute__((always_inline)) {
-    const int k0 = j * BC;
-    const bool masked = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > wq0);
-    if (!masked || j >= w_kt) return;  // tiles past the wave's last one are never used
-    const int base = k0 + 8 * hh;
+    // tiles [t_mask, w_kt) need it (tiles past the wave's last one are never used)
+    if ((uint32_t)(j - t_mask) >= n_masked) return;
+    const int base = j * BC + 8 * hh;
     // wait out the S^T MFMAs before the inline-assembly compares read their results
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0][0]));
 #pragma unroll
@@ -533,6 +590,9 @@ fa_fwd_wide_kernel(const Params p) {
       if (qb == 0 && i > 0)
         asm volatile("" ::"v"(vf[i - 1]), "v"(p_cur[0][(i - 1) / (D / 32)]),
                      "v"(p_cur[1][(i - 1) / (D / 32)]));
+      // one LDS wait per two steps: the operands of steps i and i + 1 together (read
+      // FA_W_PF and FA_W_PF - 1 steps before)
+      if (qb == 0 && i % 2 == 0 && i + 1 < NPV) asm volatile("" ::"v"(vf[i]), "v"(vf[i + 1]));
       mfma_acc_agpr<BF16>(oacc[db][qb], vf[i], p_cur[qb][st]);
       __builtin_amdgcn_sched_barrier(0);
       if (i + FA_W_PF < NPV) {
@@ -541,8 +601,7 @@ fa_fwd_wide_kernel(const Params p) {
         vf[i + FA_W_PF][2 * qb + 1] = h[1];
       }
       if (qb == 0 && i >= NPV - FA_W_PF) kf[i - (NPV - FA_W_PF)] = k_frag(kst, i - (NPV - FA_W_PF));
-      if (sc % COPY_EVERY == 1)
-        copy_step(j + R + 1, (u + 1) % R, j + R - 1, (u + R - 1) % R, sc / COPY_EVERY);
+      if (sc % COPY_EVERY == 1) copy_loop(u, sc / COPY_EVERY);
 #pragma unroll
       for (int o = FA_W_OPS.first[sc]; o < FA_W_OPS.first[sc + 1]; ++o) exp_op(s_mid, p_mid, o);
       __builtin_amdgcn_sched_barrier(0);
@@ -553,6 +612,10 @@ fa_fwd_wide_kernel(const Params p) {
     for (int sb = 0; sb < SB_N; ++sb) {
       const int sl = SC_N + sb;
       const int i = sb / 2, qb = sb % 2, kb = i % (BC / 32), ds = i / (BC / 32);
+      if (qb == 0 && i % 2 == 0 && i + 1 < NQK) {
+        asm volatile("" ::"v"(kf[i]), "v"(kf[i + 1]));
+        __builtin_amdgcn_sched_barrier(0);  // (the product must not move above the wait)
+      }
       s_new[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_new[kb][qb]);
       __builtin_amdgcn_sched_barrier(0);
       if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(kst, i + FA_W_PF);
@@ -632,6 +695,7 @@ fa_fwd_wide_kernel(const Params p) {
   // every wave is done with K_0's slot before K_R goes into it
   ring_barrier();
   copy_k(R);
+  set_m0(k_lds, (1 % R) * CHUNKS * 16);  // the loop's first copy: K_{R+1}, ring slot 1
   // everything but K_R has landed: K_2 .. K_{R-1}, V_0 .. V_2
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PW) : "memory");
   ring_barrier();
@@ -648,6 +712,9 @@ fa_fwd_wide_kernel(const Params p) {
   // S^T tiles alternate between sa and sb (tile t in sa when t is even), P tiles
   // between pa and pb likewise; with R even, the parity of j is that of u.
   for (int j0 = 0; j0 < n_kt; j0 += R) {
+    kgj = kg + (size_t)j0 * BC * D;
+    vgj = vg + (size_t)j0 * BC * D;
+    remj = kv_bytes - (uint32_t)j0 * TB;  // j0 < n_kt: tile j0 starts below the end
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int j = j0 + u;
@@ -661,7 +728,10 @@ fa_fwd_wide_kernel(const Params p) {
         if (j + 1 < w_kt) settle(j + 1, p_mid);
       } else {
 #pragma unroll
-        for (int i = 0; i < NDMA; ++i) copy_step(j + R + 1, (u + 1) % R, j + R - 1, (u + R - 1) % R, i);
+        for (int i = 0; i < NDMA; ++i) {
+          asm volatile("s_nop 0");  // the wait state after the previous copy's M0 write
+          copy_loop(u, i);
+        }
       }
       end_wait();
       loop_barrier();
