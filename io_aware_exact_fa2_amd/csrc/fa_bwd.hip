@@ -76,7 +76,9 @@ int fa_bwd_impl(const void* q, const void* k, const void* v, const void* o, cons
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
-  p.delta = static_cast<float*>(dq);  // B*H*N floats fit in dq's B*H*N*d*2 bytes (d >= 64)
+  // D and L log2(e): 2 B*H*N floats, within dq's B*H*N*d*2 bytes (d >= 64)
+  p.delta = static_cast<float*>(dq);
+  p.lse2 = p.delta + static_cast<size_t>(B) * H * N;
   p.N = N;
   p.BH = B * H;
   p.scale = scale;

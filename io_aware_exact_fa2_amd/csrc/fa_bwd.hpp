@@ -44,6 +44,11 @@
 #ifndef FA_BWD_DQ_AHEAD
 #define FA_BWD_DQ_AHEAD 2
 #endif
+// d = 128 dK/dV: the slot-scheduled kernel of fa_bwd_wide.hpp (1) or the 32-key kernel
+// here (0)
+#ifndef FA_BWD_WIDE
+#define FA_BWD_WIDE 1
+#endif
 
 namespace fa {
 
@@ -60,6 +65,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* delta;  // [BH, N] D_i = rowsum(dO * O); lives in dq's memory until dQ is written
+  float* lse2;   // [BH, N] L_i log2(e), next to delta in dq's memory
   int N;
   int BH;
   float scale;  // signed
@@ -132,8 +138,8 @@ __device__ __forceinline__ void bwd_store_rows(uint16_t* dst, const f32x16_t (&a
 
 // ---- D = rowsum(dO * O): one pass, CPR threads per row ---------------------------------
 // Written to p.delta (the dQ output's memory, as float32) for the dK/dV kernel, which
-// would otherwise recompute it for every key tile; the dQ kernel runs after it and
-// computes D for its own rows.
+// would otherwise recompute it for every key tile, with L log2(e) next to it in p.lse2;
+// the dQ kernel runs after it and computes D and reads L for its own rows.
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p) {
   using E = Elt<BF16>;
@@ -149,7 +155,10 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const BwdParams p) {
   }
 #pragma unroll
   for (int m = 1; m < CPR; m <<= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && ch == 0) p.delta[row] = acc;
+  if (row < rows && ch == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * 1.4426950408889634f;
+  }
 }
 
 // ---- dQ: one workgroup per 128 query rows -------------------------------------------
@@ -518,6 +527,16 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
 // ---- launches ------------------------------------------------------------------------
 constexpr int kBwdRows = 128;  // query rows per dQ workgroup = keys per dK/dV workgroup
 
+// The slot-scheduled dK/dV and dQ kernels at head dim 128 (fa_bwd_wide.hpp, defined in
+// the head-dim-128 translation unit); they need a nonzero scale (their causal masks set
+// scores to an infinity of the sign that gives P = 0).
+template <bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dkdv_wide_kernel(const BwdParams p);
+template <bool BF16, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dq_wide_kernel(const BwdParams p);
+
 // One backward call: three launches in stream order, D into dq's memory, dK and dV
 // (reading D), then dQ (overwriting that memory; it computes D for its own rows).
 // Explicitly instantiated per head dim in fa_bwd_d64.hip and fa_bwd_d128.hip, which
@@ -531,11 +550,25 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
                      dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s,
-                     p);
+  bool wide = false;
+  if constexpr (D == 128) {
+#if FA_BWD_WIDE
+    wide = p.c != 0.f;
+    if (wide)
+      hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<BF16, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
+                         s, p);
+#endif
+  }
+  if (!wide)
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s,
+                       p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s, p);
+  if (wide)
+    hipLaunchKernelGGL((fa_bwd_dq_wide_kernel<BF16, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

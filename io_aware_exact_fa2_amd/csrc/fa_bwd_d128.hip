@@ -6,7 +6,7 @@
 // the dK/dV kernel runs one wave per SIMD with more than 256 registers, and the default
 // scheduler issues each product's LDS operand read just before the product, leaving its
 // latency exposed; the ILP schedule issues the reads earlier.
-#include "fa_bwd.hpp"
+#include "fa_bwd_wide.hpp"
 
 namespace fa {
 template hipError_t launch_bwd<true, 128, false>(const BwdParams&, hipStream_t);

@@ -136,6 +136,40 @@ __device__ __forceinline__ u32x4_t o_chunk_read(const unsigned char* t, int r, i
   return o_swap<CPR>(r, c) ? u32x4_t{x[2], x[3], x[0], x[1]} : x;
 }
 
+// Raw buffer resource over `bytes` bytes at address a (stride 0, 32-bit format): reads
+// past the end return zeros.
+__device__ __forceinline__ u32x4_t buffer_rsrc(uint64_t a, uint32_t bytes) {
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
+}
+// min(max(x, 0), hi) on the scalar unit, for a wave-uniform x (a clamp the compiler
+// would do with v_med3 on the vector unit, leaving a buffer resource word in a vector
+// register)
+__device__ __forceinline__ uint32_t sclamp(int x, int hi /* a constant */) {
+  uint32_t r;
+  asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(x), "n"(hi) : "scc");
+  return r;
+}
+
+// HBM -> LDS copies issued as inline assembly, so the compiler's memory counter model
+// does not see them and adds no waits of its own: the kernels order them with explicit
+// vmcnt waits and barriers. They write no register. One copy: lane l's 16 (lds_copy16)
+// or 4 (lds_copy4) bytes at byte offset voff of the buffer land at LDS address lds +
+// lds_off + 16 l (or 4 l); M0 holds the LDS address, and bytes past the buffer's size
+// read as 0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4_t rsrc, uint32_t voff, uint32_t lds,
+                                           int lds_off /* a constant after unrolling */) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds), "n"(lds_off) : "m0", "scc");
+}
+__device__ __forceinline__ void lds_copy4(u32x4_t rsrc, uint32_t voff, uint32_t lds,
+                                          int lds_off /* a constant after unrolling */) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds), "n"(lds_off) : "m0", "scc");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

@@ -68,25 +68,8 @@ struct WideGeom {
   static_assert(R >= 4 && R % 2 == 0, "the ring holds the tiles of three stages");
 };
 
-// Raw buffer resource over `bytes` bytes at address a (stride 0, 32-bit format): reads
-// past the end return zeros.
-__device__ __forceinline__ u32x4_t buffer_rsrc(uint64_t a, uint32_t bytes) {
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, (uint32_t)kBufferWord3};
-}
-
-// The HBM -> LDS copies (K, V and the Q rows) are issued as inline assembly, so the
-// compiler's memory counter model does not see them and adds no waits of its own: the
-// kernel orders them with explicit vmcnt waits and its ring barrier. They write no
-// register. One 16-byte-per-lane copy: lane l's 16 bytes at byte offset voff of the
-// buffer land at LDS address lds + lds_off + 16 l (M0 holds the wave's LDS base); bytes
-// past the buffer's size read as 0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_copy16(u32x4_t rsrc, uint32_t voff, uint32_t lds,
-                                           int lds_off /* a constant after unrolling */) {
-  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(lds), "n"(lds_off) : "m0", "scc");
-}
 // The main loop's copies keep M0 one copy ahead: each issues its load with the LDS
 // address the previous one left in M0, then sets M0 to the next copy's (saving the
 // set-up and the wait state in front of every load). An LDS copy needs one instruction

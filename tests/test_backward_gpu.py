@@ -118,9 +118,11 @@ def test_backward_sequence_lengths_d64(N, causal):
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 0.02, 0.5])
-def test_backward_scale_values(scale):
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_scale_values(scale, d):
+    # at d = 128 a zero scale takes the 32-key dK/dV kernel, any other the slot-scheduled one
     for causal in (False, True):
-        _case(Workload("scale", 1, 2, 200, 64, "bf16", causal, seed=7900), scale=scale)
+        _case(Workload("scale", 1, 2, 200, d, "bf16", causal, seed=7900 + d), scale=scale)
 
 
 # ------------------------------------------------------ full-size workloads, sampled heads
