@@ -18,10 +18,10 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 # source -> options of its own. The d = 128 backward uses LLVM's iterative ILP machine
-# scheduler: its dK/dV kernel (one wave per SIMD, more than 256 registers) then issues
-# LDS operand reads further ahead of their products (measured +6 to +12% on the
-# backward); the d = 64 backward measured 3% slower with it, and the forward sources
-# schedule their loops explicitly.
+# scheduler: its 32-key dK/dV kernel (taken at a zero scale; one wave per SIMD, more than
+# 256 registers) then issues LDS operand reads further ahead of their products (measured
+# +6 to +12% on that backward); the d = 64 backward measured 3% slower with it, and the
+# forward sources and the slot-scheduled backward kernels order their loops explicitly.
 SOURCES = {
     # the forward's wide kernel unrolls four ring iterations of 64 MFMA slots each,
     # together with the rarely taken rescale path, past the default limit of forced

@@ -44,8 +44,7 @@
 #ifndef FA_BWD_DQ_AHEAD
 #define FA_BWD_DQ_AHEAD 2
 #endif
-// d = 128 dK/dV: the slot-scheduled kernel of fa_bwd_wide.hpp (1) or the 32-key kernel
-// here (0)
+// dK/dV and dQ: the slot-scheduled kernels of fa_bwd_wide.hpp (1) or the kernels here (0)
 #ifndef FA_BWD_WIDE
 #define FA_BWD_WIDE 1
 #endif
@@ -527,15 +526,13 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(const BwdParams p) {
 // ---- launches ------------------------------------------------------------------------
 constexpr int kBwdRows = 128;  // query rows per dQ workgroup = keys per dK/dV workgroup
 
-// The slot-scheduled dK/dV and dQ kernels at head dim 128 (fa_bwd_wide.hpp, defined in
-// the head-dim-128 translation unit); they need a nonzero scale (their causal masks set
-// scores to an infinity of the sign that gives P = 0).
-template <bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-fa_bwd_dkdv_wide_kernel(const BwdParams p);
-template <bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-fa_bwd_dq_wide_kernel(const BwdParams p);
+// The slot-scheduled dK/dV and dQ kernels (fa_bwd_wide.hpp, included by the translation
+// units of the head dims); they need a nonzero scale (their causal masks set scores to an
+// infinity of the sign that gives P = 0).
+template <bool BF16, int D, bool CAUSAL>
+__global__ void fa_bwd_dkdv_wide_kernel(const BwdParams p);
+template <bool BF16, int D, bool CAUSAL>
+__global__ void fa_bwd_dq_wide_kernel(const BwdParams p);
 
 // One backward call: three launches in stream order, D into dq's memory, dK and dV
 // (reading D), then dQ (overwriting that memory; it computes D for its own rows).
@@ -550,23 +547,18 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
                      dim3(static_cast<unsigned>((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bool wide = false;
-  if constexpr (D == 128) {
-#if FA_BWD_WIDE
-    wide = p.c != 0.f;
-    if (wide)
-      hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<BF16, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
-                         s, p);
-#endif
-  }
-  if (!wide)
+  const bool wide = FA_BWD_WIDE && p.c != 0.f;
+  if (wide)
+    hipLaunchKernelGGL((fa_bwd_dkdv_wide_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
+                       s, p);
+  else
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s,
                        p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (wide)
-    hipLaunchKernelGGL((fa_bwd_dq_wide_kernel<BF16, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s,
-                       p);
+    hipLaunchKernelGGL((fa_bwd_dq_wide_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
+                       s, p);
   else
     hipLaunchKernelGGL((fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s, p);
   return hipGetLastError();

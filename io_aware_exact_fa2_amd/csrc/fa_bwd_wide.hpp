@@ -1,32 +1,33 @@
-// fa_bwd_wide.hpp — dK and dV at head dim 128 for gfx950: one workgroup per 128 keys
-// (32 per wave, one wave per SIMD), the query rows streamed in 32-row blocks through a
-// ring of LDS slots, and each block's products and softmax terms in a three-stage
-// pipeline of fenced MFMA slots.
+// fa_bwd_wide.hpp — the dK/dV and dQ kernels of the backward for gfx950 at head dims 64
+// and 128: one workgroup per 128 keys (dK/dV) or 128 queries (dQ), 32 per wave, the other
+// side's rows streamed in 32-row blocks through a ring of LDS slots, and each block's
+// products and softmax terms in a three-stage pipeline of fenced MFMA slots.
 //
-// What it computes is the dK/dV half of the chain rule in fa_bwd.hpp ([P1]
-// currybab.bearblog.dev, FA2 section: the backward recomputes P_ij = exp(S_ij - L_i)
-// block by block from the saved L instead of storing P): for the wave's 32 keys (on the
-// lanes) and every query block,
+// What they compute is the chain rule of fa_bwd.hpp ([P1] currybab.bearblog.dev, FA2
+// section: the backward recomputes P_ij = exp(S_ij - L_i) block by block from the saved
+// L instead of storing P). dK/dV: for the wave's 32 keys (on the lanes) and every query
+// block,
 //     S = Q K^T, dP = dO V^T, P = exp2(S c - L log2 e), dS = P (dP - D),
 //     dV^T += dO^T P,  dK^T += Q^T dS,
 // and at the end dK = scale dK. D_i = rowsum(dO * O)_i and L_i log2(e) come from the
-// D pass (fa_bwd_delta_kernel).
+// D pass (fa_bwd_delta_kernel). dQ: see fa_bwd_dq_wide_kernel below.
 //
-// Why this kernel. The 32-key kernel of fa_bwd.hpp left the order of its products and
-// LDS operand reads to the compiler, and each product waited for a read issued just
-// before it: the matrix core was busy about a third of the time at the chip's full
-// clock. Here iteration t issues, one MFMA per slot, the 16 dV/dK products of query
-// block t, then the 16 S/dP products of block t+2, and between them the softmax terms of
-// block t+1 (80 VALU ops per lane, spread over the slots by a compile-time table); every
-// operand read runs FA_BW_PF steps ahead of its product. Block b's rows reach LDS by
-// buffer-to-LDS copies issued in iteration b-5 into ring slot b % 6 (16 KB: Q and dO),
-// with its L log2(e) and D (256 bytes each); one barrier per iteration.
+// Why these kernels. The kernels of fa_bwd.hpp left the order of their products and LDS
+// operand reads to the compiler, and each product waited for a read issued just before
+// it: the dK/dV matrix core was busy about a third of the time at the chip's full clock.
+// Here dK/dV iteration t issues, one MFMA per slot, the dV/dK products of query block t
+// (16 at d = 128), then the S/dP products of block t+2 (16), and between them the softmax
+// terms of block t+1 (80 VALU ops per lane, spread over the slots by a compile-time
+// table); every operand read runs FA_BW_PF steps ahead of its product and the wave waits
+// for LDS once per two steps. Block b's rows reach LDS by buffer-to-LDS copies issued in
+// iteration b-5 into ring slot b % 6 (Q and dO: 16 KB at d = 128), with its L log2(e) and
+// D (256 bytes each); one barrier per iteration.
 //
 // Rows past N need no mask: their copies read zeros (Q, dO, L and D), so S = dP = 0,
 // P = 1 and dS = 0, and they add dO^T P = 0 and Q^T dS = 0. Keys past N (lanes) compute
 // columns that are not stored. Under the causal mask, a block that reaches past the
 // wave's first key gets S = -inf (c > 0; +inf when c < 0) above the diagonal, so P = 0
-// and dS = 0 there; c = 0 takes the 32-key kernel.
+// and dS = 0 there; c = 0 takes the kernels of fa_bwd.hpp.
 #pragma once
 
 #include "fa_bwd.hpp"
@@ -54,8 +55,9 @@ struct BwdOpSched {
   int n;
   int first[65];  // ops [first[s], first[s + 1]) go into slot s
 };
-template <int NSLOT, int FIRST, int PF, int NC>
+template <int NSLOT, int FIRST, int PF, int NC, int NAS>
 constexpr BwdOpSched make_bwd_op_sched(bool two_blocks) {
+  // two_blocks: NSLOT = 2 NAS dV/dK slots, then the S/dP slots; else S/dP slots only
   BwdOpSched t{};
   int n = 0;
   const int ops_of[4][4] = {{0, 1, 4, 5}, {2, 3, -1, -1}, {6, 7, 8, -1}, {9, -1, -1, -1}};
@@ -71,14 +73,15 @@ constexpr BwdOpSched make_bwd_op_sched(bool two_blocks) {
   long total = 0;
   for (int sl = 0; sl < NSLOT; ++sl) {
     int f = 4;  // the MFMA
-    if (two_blocks && sl < 16) {  // dV/dK block: transposed reads, L/D reads, copies
+    const int nbs = two_blocks ? (NSLOT - 2 * NAS) / 2 : NSLOT / 2;  // S/dP steps
+    if (two_blocks && sl < 2 * NAS) {  // dV/dK block: transposed reads, L/D reads, copies
       const int i = sl / 2;
-      f += (i + PF < 8) ? 40 : 8;
+      f += (i + PF < NAS) ? 40 : 8;
       if (sl < 2) f += 32;
       if (sl % 2 == 1 && sl / 2 < NC) f += 18;
     } else {  // S/dP block: row reads, the next iteration's transposed reads
-      const int i = (two_blocks ? sl - 16 : sl) / 2;
-      f += (i + PF < 8) ? 8 : (two_blocks ? 40 : 0);
+      const int i = (two_blocks ? sl - 2 * NAS : sl) / 2;
+      f += (i + PF < nbs) ? 8 : (two_blocks ? 40 : 0);
     }
     fixed[sl] = f;
     total += f;
@@ -106,12 +109,18 @@ constexpr BwdOpSched make_bwd_op_sched(bool two_blocks) {
   t.first[NSLOT] = n;
   return t;
 }
-// the loop: 32 slots, ops from slot 3 (the block's L and D are read in slots 0 and 1);
-// the prologue: the 16 S/dP slots of block 1 carry the softmax of block 0
-template <int PF, int NC>
-constexpr BwdOpSched kBwdLoopOps = make_bwd_op_sched<32, 3, PF, NC>(true);
-template <int PF, int NC>
-constexpr BwdOpSched kBwdPrologueOps = make_bwd_op_sched<16, 2, PF, NC>(false);
+// the loop: 2 NAS + 2 NBS slots, ops from slot 3 (the block's L and D are read in slots 0
+// and 1); the prologue: the 2 NBS S/dP slots of block 1 carry the softmax of block 0
+template <int PF, int NC, int NAS, int NBS>
+constexpr BwdOpSched kBwdLoopOps = make_bwd_op_sched<2 * NAS + 2 * NBS, 3, PF, NC, NAS>(true);
+template <int PF, int NC, int NAS, int NBS>
+constexpr BwdOpSched kBwdPrologueOps = make_bwd_op_sched<2 * NBS, 2, PF, NC, NAS>(false);
+
+// waves per SIMD that the slot-scheduled backward kernels are compiled for: one, except
+// dQ at head dim 64, which fits two in 256 registers (dK/dV at 64 does not: bounded to two
+// waves it crashed the compiler's AGPR-copy rewrite)
+template <int D> constexpr int kBwdWavesKV = 1;
+template <int D> constexpr int kBwdWavesQ = D == 64 ? 2 : 1;
 
 // x = (c >= lo) ? x : m, with c a constant after unrolling (m from a register)
 __device__ __forceinline__ float keep_if_ge(float x, int c, int lo, float m) {
@@ -120,16 +129,21 @@ __device__ __forceinline__ float keep_if_ge(float x, int c, int lo, float m) {
   return x;
 }
 
-template <bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(kBwdWavesKV<D>, kBwdWavesKV<D>)))
 fa_bwd_dkdv_wide_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  constexpr int D = 128, CPR = D / 8, NDS = D / 16, NW = 4, QB = 32, R = 6;
-  constexpr int SLOT = QB * CPR;  // 16-byte chunks of one block's Q (or dO) rows: 8 KB
+  constexpr int CPR = D / 8, NDS = D / 16, NDB = D / 32, NW = 4, QB = 32, R = 6;
+  constexpr int SLOT = QB * CPR;  // 16-byte chunks of one block's Q (or dO) rows
+  constexpr int PPW = SLOT / 64 / NW;  // 1 KB pieces per wave, block and tensor
+  constexpr int NAS = 2 * NDB;    // dV/dK steps (two products each) per block
   constexpr int PF = FA_BW_PF;
-  constexpr int NC = 5;           // copies per wave and block: L2 or D, 2 of Q, 2 of dO
+  constexpr int NC = 1 + 2 * PPW; // copies per wave and block: L2 or D, then Q, then dO
+  static_assert(D == 64 || D == 128, "head dims");
+  static_assert(PF <= NAS && PF <= NDS && NC <= NAS, "read-ahead and copies fit the blocks");
   constexpr int AHEAD = 5;        // block t + AHEAD is copied in iteration t
-  static_assert(PF >= 1 && PF <= 4, "operand reads a few steps ahead");
+  static_assert(PF >= 1 && 4 * PF <= 15, "operand reads a few steps ahead (lgkmcnt holds 15)");
   static_assert(R % 2 == 0 && R >= AHEAD + 1, "ring: even (tile buffers alternate) and deep enough");
   __shared__ __attribute__((aligned(1024))) u32x4_t qring[R * SLOT];
   __shared__ __attribute__((aligned(1024))) u32x4_t dring[R * SLOT];
@@ -177,12 +191,13 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
 
   // ---- copies: block g (rows 32 g ..) into ring slot sl. Copy 0 moves 64 floats of L
   // log2(e) (even waves) or of D (odd waves) from row 32 g on (the second 32 are not
-  // read; a pair of waves copies the same bytes); copies 1, 2 move 1 KB pieces wid and
-  // wid + 4 of the Q rows, 3, 4 those of the dO rows: lane l of piece c writes chunk
-  // 64 c + l of the slot and fetches the logical chunk the swizzle puts there. -------
-  uint32_t cvoff[2];
+  // read; a pair of waves copies the same bytes); copies 1 .. PPW move 1 KB pieces wid,
+  // wid + 4, .. of the Q rows, the next PPW those of the dO rows: lane l of piece c
+  // writes chunk 64 c + l of the slot and fetches the logical chunk the swizzle puts
+  // there. ---------------------------------------------------------------------------
+  uint32_t cvoff[PPW];
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
+  for (int cc = 0; cc < PPW; ++cc) {
     const int f = (wid + NW * cc) * 64 + lane, row = f / CPR, ph = f % CPR;
     cvoff[cc] = (uint32_t)(row * D + (ph ^ swz_b<D>(row)) * 8) * 2u;
   }
@@ -200,8 +215,8 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
                 (uint32_t)lane * 4u, ld_lds, sl * 256);
     } else {
       const uint32_t nb2 = sclamp(left, QB) * (uint32_t)(D * 2);
-      const int piece = (cc - 1) % 2;
-      const bool is_q = cc <= 2;
+      const int piece = (cc - 1) % PPW;
+      const bool is_q = cc <= PPW;
       const uint16_t* src = (is_q ? p.q : p.dout) + head + (size_t)row0 * D;
       lds_copy16(buffer_rsrc((uint64_t)(uintptr_t)src, nb2), cvoff[piece], is_q ? q_lds : d_lds,
                  sl * SLOT * 16 + piece * NW * 1024);
@@ -226,9 +241,9 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
       asm volatile("" : "+v"(raddr[0][ds]), "+v"(raddr[1][ds]));
     }
   }
-  uint32_t taddr[2][D / 32][2];  // [w: dO, Q][db][h]
+  uint32_t taddr[2][NDB][2];  // [w: dO, Q][db][h]
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t o = bwd_tr_off<D>(lane, db, h);
@@ -242,14 +257,14 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
   auto row_op = [&](int w, int sl, int ds) __attribute__((always_inline)) {
     return *(lds_u32x4_t*)(uintptr_t)(raddr[w][ds] + (uint32_t)(sl * SLOT * 16));
   };
-  // transposed operand of step i (16-query half i / 4, head dims 32 (i % 4) ..) of block
-  // slot sl (w 0: dO, 1: Q): rows 16 (i / 4) .., two 4-row halves
+  // transposed operand of step i (16-query half i / NDB, head dims 32 (i % NDB) ..) of
+  // block slot sl (w 0: dO, 1: Q): rows 16 (i / NDB) .., two 4-row halves
   auto tr_op = [&](int w, int sl, int i) __attribute__((always_inline)) {
-    const uint32_t off = (uint32_t)(sl * SLOT * 16 + (i / 4) * 16 * CPR * 16);
+    const uint32_t off = (uint32_t)(sl * SLOT * 16 + (i / NDB) * 16 * CPR * 16);
     const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(uintptr_t)(taddr[w][i % 4][0] + off));
+        (lds_s16x4_t*)(uintptr_t)(taddr[w][i % NDB][0] + off));
     const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(uintptr_t)(taddr[w][i % 4][1] + off));
+        (lds_s16x4_t*)(uintptr_t)(taddr[w][i % NDB][1] + off));
     const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
     return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
   };
@@ -305,7 +320,7 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
   };
 
   // ---- one iteration: dV, dK of block t; softmax terms of block t+1; S, dP of block t+2
-  constexpr BwdOpSched OPS = kBwdLoopOps<PF, NC>;
+  constexpr BwdOpSched OPS = kBwdLoopOps<PF, NC, NAS, NDS>;
   u32x4_t anext[PF][2];  // the first transposed operands of the next iteration
   auto iteration = [&](int u, int t, f32x16_t& s_new, f32x16_t& dp_new, const f32x16_t& s_mid,
                        const f32x16_t& dp_mid, u32x4_t (&p_mid)[2], u32x4_t (&ds_mid)[2],
@@ -314,22 +329,22 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
     // ring slots: block t in slot u = t % R
     const int sl0 = u, sl1 = (u + 1) % R, sl2 = (u + 2) % R, slc = (u + AHEAD) % R;
     f32x4_t lv[4], dv4[4];
-    u32x4_t aop[8][2], bop[8][2];
+    u32x4_t aop[NAS][2], bop[NDS][2];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       aop[i][0] = anext[i][0];
       aop[i][1] = anext[i][1];
     }
-    // dV^T += dO^T P and dK^T += Q^T dS of block t: step i (16-query half i / 4, head-dim
-    // block i % 4), slot w = 0: dV, 1: dK
+    // dV^T += dO^T P and dK^T += Q^T dS of block t: step i (16-query half i / NDB,
+    // head-dim block i % NDB), slot w = 0: dV, 1: dK
 #pragma unroll
-    for (int sa = 0; sa < 16; ++sa) {
-      const int i = sa / 2, w = sa % 2, hq = i / 4, db = i % 4;
+    for (int sa = 0; sa < 2 * NAS; ++sa) {
+      const int i = sa / 2, w = sa % 2, hq = i / NDB, db = i % NDB;
       // keep the previous step's sources live until this step (the inline-assembly MFMAs
       // read them over several cycles)
       if (w == 0 && i > 0)
-        asm volatile("" ::"v"(aop[i - 1][0]), "v"(aop[i - 1][1]), "v"(p_cur[(i - 1) / 4]),
-                     "v"(ds_cur[(i - 1) / 4]));
+        asm volatile("" ::"v"(aop[i - 1][0]), "v"(aop[i - 1][1]), "v"(p_cur[(i - 1) / NDB]),
+                     "v"(ds_cur[(i - 1) / NDB]));
 #if FA_BW_PAIR
       // one LDS wait per two steps: the operands of steps i and i + 1 together
       if (w == 0 && i % 2 == 0)
@@ -338,8 +353,8 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
       if (w == 0) mfma_acc_agpr<BF16>(dv[db], aop[i][0], p_cur[hq]);
       else mfma_acc_agpr<BF16>(dk[db], aop[i][1], ds_cur[hq]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + PF < 8) aop[i + PF][w] = tr_op(w, sl0, i + PF);
-      else bop[i + PF - 8][w] = row_op(w, sl2, i + PF - 8);
+      if (i + PF < NAS) aop[i + PF][w] = tr_op(w, sl0, i + PF);
+      else bop[i + PF - NAS][w] = row_op(w, sl2, i + PF - NAS);
       if (sa == 0) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) lv[g] = ld_op(lring, sl1, g);
@@ -353,12 +368,12 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
         soft_op(OPS, s_mid, dp_mid, lv, dv4, p_mid, ds_mid, o);
       __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("" ::"v"(aop[7][0]), "v"(aop[7][1]), "v"(p_cur[1]), "v"(ds_cur[1]));
+    asm volatile("" ::"v"(aop[NAS - 1][0]), "v"(aop[NAS - 1][1]), "v"(p_cur[1]), "v"(ds_cur[1]));
     // S = Q K^T and dP = dO V^T of block t+2: step i (16 head dims), slot w = 0: S, 1: dP
     zero16(s_new);
     zero16(dp_new);
 #pragma unroll
-    for (int sb = 0; sb < 16; ++sb) {
+    for (int sb = 0; sb < 2 * NDS; ++sb) {
       const int i = sb / 2, w = sb % 2;
 #if FA_BW_PAIR
       if (w == 0 && i % 2 == 0) {
@@ -369,10 +384,10 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
       if (w == 0) s_new = E::mfma(bop[i][0], kf[i], s_new);
       else dp_new = E::mfma(bop[i][1], vf[i], dp_new);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + PF < 8) bop[i + PF][w] = row_op(w, sl2, i + PF);
-      else anext[i + PF - 8][w] = tr_op(w, sl1, i + PF - 8);
+      if (i + PF < NDS) bop[i + PF][w] = row_op(w, sl2, i + PF);
+      else anext[i + PF - NDS][w] = tr_op(w, sl1, i + PF - NDS);
 #pragma unroll
-      for (int o = OPS.first[16 + sb]; o < OPS.first[16 + sb + 1]; ++o)
+      for (int o = OPS.first[2 * NAS + sb]; o < OPS.first[2 * NAS + sb + 1]; ++o)
         soft_op(OPS, s_mid, dp_mid, lv, dv4, p_mid, ds_mid, o);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -404,7 +419,7 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
       lv[g] = ld_op(lring, 0, g);
       dv4[g] = ld_op(dlring, 0, g);
     }
-    constexpr BwdOpSched POPS = kBwdPrologueOps<PF, NC>;
+    constexpr BwdOpSched POPS = kBwdPrologueOps<PF, NC, NAS, NDS>;
     u32x4_t bq[NDS][2];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
@@ -414,12 +429,12 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
     zero16(sB);
     zero16(dB);
 #pragma unroll
-    for (int sb = 0; sb < 16; ++sb) {
+    for (int sb = 0; sb < 2 * NDS; ++sb) {
       const int i = sb / 2, w = sb % 2;
       if (w == 0) sB = E::mfma(bq[i][0], kf[i], sB);
       else dB = E::mfma(bq[i][1], vf[i], dB);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + PF < 8) bq[i + PF][w] = row_op(w, 1, i + PF);
+      if (i + PF < NDS) bq[i + PF][w] = row_op(w, 1, i + PF);
 #pragma unroll
       for (int o = POPS.first[sb]; o < POPS.first[sb + 1]; ++o)
         soft_op(POPS, sA, dA, lv, dv4, pA, dsA, o);
@@ -469,35 +484,36 @@ fa_bwd_dkdv_wide_kernel(const BwdParams p) {
 
 namespace fa {
 
-// ---- dQ at head dim 128 ---------------------------------------------------------------
-// One workgroup per 128 query rows (32 per wave, one wave per SIMD); the keys stream in
-// 32-key blocks through a ring of LDS slots (K and V rows, 16 KB per block). For the
-// wave's queries (on the lanes) and every key block,
+// ---- dQ ------------------------------------------------------------------------------
+// One workgroup per 128 query rows (32 per wave); the keys stream in 32-key blocks
+// through a ring of LDS slots (K and V rows, 16 KB per block at d = 128). For the wave's
+// queries (on the lanes) and every key block,
 //     S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), P^T = exp2(S^T c - L log2 e),
 //     dQ^T += K^T dS^T,
-// and at the end dQ = scale dQ. Iteration t issues the 8 dQ products of key block t,
-// then the 16 S/dP products of block t+2, and between them the softmax terms of block
-// t+1 (72 VALU ops per lane: L and D are the lane's own). An MFMA slot's operand is read
+// and at the end dQ = scale dQ. Iteration t issues the dQ products of key block t (8 at
+// d = 128), then the S/dP products of block t+2 (16), and between them the softmax terms
+// of block t+1 (72 VALU ops per lane: L and D are the lane's own). An MFMA slot's operand is read
 // FA_BQ_PS slots ahead, and the wave waits for LDS once per two slots. Block b is copied
 // in iteration b-5 into slot b % 6; one barrier per iteration.
 //
 // Keys past N need no mask: their K and V rows read as zeros, so dS^T may be nonzero
 // there but meets a zero K^T column. Queries past N (lanes) are computed on row N - 1 and
 // not stored. Under the causal mask, scores of keys after the lane's query are set to
-// the infinity that gives P = 0 (c != 0; c = 0 takes the 32-query kernel).
+// the infinity that gives P = 0 (c != 0; c = 0 takes the kernel of fa_bwd.hpp).
 #ifndef FA_BQ_PS
 #define FA_BQ_PS 6  // MFMA slots an operand read runs ahead
 #endif
 
 // The softmax terms of one key block, 9 ops per pair of registers (2v, 2v+1): 0-1 FMA,
 // 2-3 exponentials, 4-5 dP - D, 6-7 the products, 8 the 16-bit pack of dS; staged as in
-// make_bwd_op_sched and spread over the 24 slots by estimated issue time.
+// make_bwd_op_sched and spread over the NSL slots (NA dQ slots, then the S/dP slots) by
+// estimated issue time.
 struct DqOpSched {
   int code[72];  // 10 * pair + op
   int n;
   int first[25];
 };
-template <int PS, int NC>
+template <int PS, int NC, int NA, int NSL>
 constexpr DqOpSched make_dq_op_sched() {
   DqOpSched t{};
   int n = 0;
@@ -512,20 +528,20 @@ constexpr DqOpSched make_dq_op_sched() {
   const int op_cost[9] = {11, 11, 24, 24, 10, 10, 10, 10, 11};
   int fixed[24] = {};
   long total = 0;
-  for (int sl = 0; sl < 24; ++sl) {
+  for (int sl = 0; sl < NSL; ++sl) {
     const int rd = sl + PS;  // the slot whose operand this slot reads
-    int f = 4 + ((rd < 8 || rd >= 24) ? 40 : 8);
-    if (sl < 8 && sl % 2 == 1 && sl / 2 < NC) f += 18;
+    int f = 4 + ((rd < NA || rd >= NSL) ? 40 : 8);
+    if (sl < NA && sl % 2 == 1 && sl / 2 < NC) f += 18;
     fixed[sl] = f;
     total += f;
   }
   for (int i = 0; i < n; ++i) total += op_cost[t.code[i] % 10];
   long cum = 0;
   int o = 0;
-  for (int sl = 0; sl < 24; ++sl) {
+  for (int sl = 0; sl < NSL; ++sl) {
     t.first[sl] = o;
     cum += fixed[sl];
-    const long target = total * (sl + 1) / 24;
+    const long target = total * (sl + 1) / NSL;
     while (o < n) {
       const int c = op_cost[t.code[o] % 10];
       if (cum + c <= target || (cum + c - target) < (target - cum)) {
@@ -536,22 +552,28 @@ constexpr DqOpSched make_dq_op_sched() {
       }
     }
   }
-  t.first[24] = n;
+  t.first[NSL] = n;
   return t;
 }
-template <int PS, int NC>
-constexpr DqOpSched kDqOps = make_dq_op_sched<PS, NC>();
+template <int PS, int NC, int NA, int NSL>
+constexpr DqOpSched kDqOps = make_dq_op_sched<PS, NC, NA, NSL>();
 
-template <bool BF16, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool BF16, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(kBwdWavesQ<D>, kBwdWavesQ<D>)))
 fa_bwd_dq_wide_kernel(const BwdParams p) {
   using E = Elt<BF16>;
-  constexpr int D = 128, CPR = D / 8, NDS = D / 16, NW = 4, KB = 32, R = 6, AHEAD = 5;
-  constexpr int SLOT = KB * CPR;  // 16-byte chunks of one block's K (or V) rows: 8 KB
-  constexpr int NC = 4;           // copies per wave and block: 2 of K, 2 of V
-  constexpr int PS = FA_BQ_PS;
-  constexpr int NSL = 24;         // MFMA slots per iteration: 8 dQ, then 8 x (S, dP)
-  static_assert(PS >= 2 && PS <= 8 && PS % 2 == 0, "operands read a few (even) slots ahead");
+  constexpr int CPR = D / 8, NDS = D / 16, NDB = D / 32, NW = 4, KB = 32, R = 6, AHEAD = 5;
+  constexpr int SLOT = KB * CPR;  // 16-byte chunks of one block's K (or V) rows
+  constexpr int PPW = SLOT / 64 / NW;  // 1 KB pieces per wave, block and tensor
+  constexpr int NC = 2 * PPW;     // copies per wave and block: K, then V
+  constexpr int NA = 2 * NDB;     // dQ slots per iteration (then NDS x (S, dP))
+  constexpr int NSL = NA + 2 * NDS;
+  constexpr int PS = FA_BQ_PS < NA ? FA_BQ_PS : NA;
+  static_assert(D == 64 || D == 128, "head dims");
+  static_assert(NC <= NA / 2 + NA % 2 && NSL % 2 == 0, "copies fit the dQ slots");
+  static_assert(PS >= 2 && 2 * PS <= 15 && PS % 2 == 0,
+                "operands read a few (even) slots ahead (lgkmcnt holds 15)");
   static_assert(R % 2 == 0 && R >= AHEAD + 1, "ring: even and deep enough");
   __shared__ __attribute__((aligned(1024))) u32x4_t kring[R * SLOT];
   __shared__ __attribute__((aligned(1024))) u32x4_t vring[R * SLOT];
@@ -593,13 +615,13 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
 
-  // ---- copies: block g (keys 32 g ..) into ring slot sl: copies 0, 1 move 1 KB pieces
-  // wid and wid + 4 of the K rows, 2, 3 those of the V rows (lane l of piece c writes
-  // chunk 64 c + l of the slot and fetches the logical chunk the swizzle puts there);
-  // rows past N read as zeros -----------------------------------------------------------
-  uint32_t cvoff[2];
+  // ---- copies: block g (keys 32 g ..) into ring slot sl: copies 0 .. PPW - 1 move 1 KB
+  // pieces wid, wid + 4, .. of the K rows, the next PPW those of the V rows (lane l of
+  // piece c writes chunk 64 c + l of the slot and fetches the logical chunk the swizzle
+  // puts there); rows past N read as zeros --------------------------------------------------
+  uint32_t cvoff[PPW];
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
+  for (int cc = 0; cc < PPW; ++cc) {
     const int f = (wid + NW * cc) * 64 + lane, row = f / CPR, ph = f % CPR;
     cvoff[cc] = (uint32_t)(row * D + (ph ^ swz_b<D>(row)) * 8) * 2u;
   }
@@ -608,8 +630,8 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
   auto copy = [&](int g, int sl, int cc) __attribute__((always_inline)) {
     const int row0 = g * KB;
     const uint32_t nbytes = sclamp(N - row0, KB) * (uint32_t)(D * 2);
-    const int piece = cc % 2;
-    const bool is_k = cc < 2;
+    const int piece = cc % PPW;
+    const bool is_k = cc < PPW;
     const uint16_t* src = (is_k ? p.k : p.v) + head + (size_t)row0 * D;
     lds_copy16(buffer_rsrc((uint64_t)(uintptr_t)src, nbytes), cvoff[piece], is_k ? k_lds : v_lds,
                sl * SLOT * 16 + piece * NW * 1024);
@@ -627,34 +649,34 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
       asm volatile("" : "+v"(raddr[0][ds]), "+v"(raddr[1][ds]));
     }
   }
-  uint32_t taddr[D / 32][2];  // transposed K: [db][h]
+  uint32_t taddr[NDB][2];  // transposed K: [db][h]
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       taddr[db][h] = (uint32_t)(uintptr_t)kring + bwd_tr_off<D>(lane, db, h);
       asm volatile("" : "+v"(taddr[db][h]));
     }
   typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
-  // the A operand of slot s of an iteration: s < 8, dQ step s (16-key half s / 4, head
-  // dims 32 (s % 4) ..) from K^T of slot slt; s >= 8, the K (even) or V (odd) rows of
-  // head-dim step (s - 8) / 2 of slot slr
+  // the A operand of slot s of an iteration: s < NA, dQ step s (16-key half s / NDB,
+  // head dims 32 (s % NDB) ..) from K^T of slot slt; s >= NA, the K (even) or V (odd)
+  // rows of head-dim step (s - NA) / 2 of slot slr
   auto operand = [&](int s, int slt, int slr) __attribute__((always_inline)) {
-    if (s < 8) {
-      const uint32_t off = (uint32_t)(slt * SLOT * 16 + (s / 4) * 16 * CPR * 16);
+    if (s < NA) {
+      const uint32_t off = (uint32_t)(slt * SLOT * 16 + (s / NDB) * 16 * CPR * 16);
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(uintptr_t)(taddr[s % 4][0] + off));
+          (lds_s16x4_t*)(uintptr_t)(taddr[s % NDB][0] + off));
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(uintptr_t)(taddr[s % 4][1] + off));
+          (lds_s16x4_t*)(uintptr_t)(taddr[s % NDB][1] + off));
       const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
       return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
     }
-    const int w = (s - 8) % 2, ds = (s - 8) / 2;
+    const int w = (s - NA) % 2, ds = (s - NA) / 2;
     return *(lds_u32x4_t*)(uintptr_t)(raddr[w][ds] + (uint32_t)(slr * SLOT * 16));
   };
 
   // ---- the softmax terms of one block ---------------------------------------------------
-  constexpr DqOpSched OPS = kDqOps<PS, NC>;
+  constexpr DqOpSched OPS = kDqOps<PS, NC, NA, NSL>;
   float xq[2][2], dq3[3][2], pq[2][2], eq[2][2];
   auto soft_op = [&](const f32x16_t& s, const f32x16_t& dp, u32x4_t (&dsop)[2], int o)
       __attribute__((always_inline)) {
@@ -715,24 +737,24 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
         asm volatile("" ::"v"(opd[s]), "v"(opd[s + 1]));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (s < 8) {
+      if (s < NA) {
         // keep the previous step's sources live until this step (the inline-assembly
         // MFMAs read them over several cycles)
-        if (s > 0) asm volatile("" ::"v"(opd[s - 1]), "v"(ds_cur[(s - 1) / 4]));
-        mfma_acc_agpr<BF16>(dq[s % 4], opd[s], ds_cur[s / 4]);
-      } else if ((s - 8) % 2 == 0) {
-        s_new = E::mfma(opd[s], qf[(s - 8) / 2], s_new);
+        if (s > 0) asm volatile("" ::"v"(opd[s - 1]), "v"(ds_cur[(s - 1) / NDB]));
+        mfma_acc_agpr<BF16>(dq[s % NDB], opd[s], ds_cur[s / NDB]);
+      } else if ((s - NA) % 2 == 0) {
+        s_new = E::mfma(opd[s], qf[(s - NA) / 2], s_new);
       } else {
-        dp_new = E::mfma(opd[s], dof[(s - 8) / 2], dp_new);
+        dp_new = E::mfma(opd[s], dof[(s - NA) / 2], dp_new);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (s + PS < NSL) opd[s + PS] = operand(s + PS, sl0, sl2);
       else onext[s + PS - NSL] = operand(s + PS - NSL, sl1, sl1);
-      if (s < 8 && s % 2 == 1 && s / 2 < NC) copy(t + AHEAD, slc, s / 2);
+      if (s < NA && s % 2 == 1 && s / 2 < NC) copy(t + AHEAD, slc, s / 2);
 #pragma unroll
       for (int o = OPS.first[s]; o < OPS.first[s + 1]; ++o) soft_op(s_mid, dp_mid, ds_mid, o);
       __builtin_amdgcn_sched_barrier(0);
-      if (s == 7) asm volatile("" ::"v"(opd[7]), "v"(ds_cur[1]));
+      if (s == NA - 1) asm volatile("" ::"v"(opd[NA - 1]), "v"(ds_cur[1]));
     }
     mask(s_new, t + 2);
   };
@@ -753,14 +775,14 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
   zero16(dB);
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) {
-    sA = E::mfma(operand(8 + 2 * ds, 0, 0), qf[ds], sA);
-    dA = E::mfma(operand(9 + 2 * ds, 0, 0), dof[ds], dA);
+    sA = E::mfma(operand(NA + 2 * ds, 0, 0), qf[ds], sA);
+    dA = E::mfma(operand(NA + 1 + 2 * ds, 0, 0), dof[ds], dA);
   }
   mask(sA, 0);
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) {
-    sB = E::mfma(operand(8 + 2 * ds, 0, 1), qf[ds], sB);
-    dB = E::mfma(operand(9 + 2 * ds, 0, 1), dof[ds], dB);
+    sB = E::mfma(operand(NA + 2 * ds, 0, 1), qf[ds], sB);
+    dB = E::mfma(operand(NA + 1 + 2 * ds, 0, 1), dof[ds], dB);
   }
 #pragma unroll
   for (int o = 0; o < OPS.n; ++o) soft_op(sA, dA, dsA, o);
