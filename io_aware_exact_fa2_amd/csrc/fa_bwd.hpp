@@ -533,6 +533,14 @@ template <bool BF16, int D, bool CAUSAL>
 __global__ void fa_bwd_dkdv_wide_kernel(const BwdParams p);
 template <bool BF16, int D, bool CAUSAL>
 __global__ void fa_bwd_dq_wide_kernel(const BwdParams p);
+// query blocks of 32 per wave in that dQ kernel at head dim 128. Two (each K, K^T or V
+// operand read from LDS then serves two products, as in the forward's wide kernel) passed
+// every backward test but measured +0.7% without the causal mask and -20% with it, where
+// the compiler spilled registers to scratch inside the loop; so one.
+#ifndef FA_BQ_QB128
+#define FA_BQ_QB128 1
+#endif
+template <int D> constexpr int kDqBlocks = D == 128 ? FA_BQ_QB128 : 1;
 
 // One backward call: three launches in stream order, D into dq's memory, dK and dV
 // (reading D), then dQ (overwriting that memory; it computes D for its own rows).
@@ -556,9 +564,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
                        p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  constexpr int qrows = 128 * kDqBlocks<D>;  // query rows per workgroup of that kernel
   if (wide)
-    hipLaunchKernelGGL((fa_bwd_dq_wide_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0,
-                       s, p);
+    hipLaunchKernelGGL((fa_bwd_dq_wide_kernel<BF16, D, CAUSAL>),
+                       dim3((p.N + qrows - 1) / qrows * p.BH), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((fa_bwd_dq_kernel<BF16, D, CAUSAL>), dim3(tiles * p.BH), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -501,37 +501,45 @@ namespace fa {
 // not stored. Under the causal mask, scores of keys after the lane's query are set to
 // the infinity that gives P = 0 (c != 0; c = 0 takes the kernel of fa_bwd.hpp).
 #ifndef FA_BQ_PS
-#define FA_BQ_PS 6  // MFMA slots an operand read runs ahead
+#define FA_BQ_PS 6  // operand slots an operand read runs ahead
 #endif
 
-// The softmax terms of one key block, 9 ops per pair of registers (2v, 2v+1): 0-1 FMA,
-// 2-3 exponentials, 4-5 dP - D, 6-7 the products, 8 the 16-bit pack of dS; staged as in
-// make_bwd_op_sched and spread over the NSL slots (NA dQ slots, then the S/dP slots) by
+
+// The softmax terms of the wave's query blocks for one key block, 9 ops per pair of
+// registers (2v, 2v+1 of query block v / 8): 0-1 FMA, 2-3 exponentials, 4-5 dP - D, 6-7
+// the products, 8 the 16-bit pack of dS; staged as in make_bwd_op_sched and spread over
+// the MFMA slots (NA dQ operand slots, then the S/dP operand slots, NQB products each) by
 // estimated issue time.
 struct DqOpSched {
-  int code[72];  // 10 * pair + op
+  int code[144];  // 10 * pair + op
   int n;
-  int first[25];
+  int first[49];
 };
-template <int PS, int NC, int NA, int NSL>
+template <int PS, int NC, int NA, int NOP, int NQB>
 constexpr DqOpSched make_dq_op_sched() {
   DqOpSched t{};
   int n = 0;
+  const int np = 8 * NQB;
   const int ops_of[4][4] = {{0, 1, 4, 5}, {2, 3, -1, -1}, {6, 7, -1, -1}, {8, -1, -1, -1}};
-  for (int k = 0; k < 8 + 3; ++k)
+  for (int k = 0; k < np + 3; ++k)
     for (int st = 0; st < 4; ++st) {
       const int v = k - st;
-      if (v < 0 || v >= 8) continue;
+      if (v < 0 || v >= np) continue;
       for (int q = 0; q < 4 && ops_of[st][q] >= 0; ++q) t.code[n++] = 10 * v + ops_of[st][q];
     }
   t.n = n;
   const int op_cost[9] = {11, 11, 24, 24, 10, 10, 10, 10, 11};
-  int fixed[24] = {};
+  constexpr int NSL = NOP * NQB;
+  int fixed[48] = {};
   long total = 0;
   for (int sl = 0; sl < NSL; ++sl) {
-    const int rd = sl + PS;  // the slot whose operand this slot reads
-    int f = 4 + ((rd < NA || rd >= NSL) ? 40 : 8);
-    if (sl < NA && sl % 2 == 1 && sl / 2 < NC) f += 18;
+    const int so = sl / NQB;  // operand slot
+    int f = 4;
+    if (sl % NQB == 0) {
+      const int rd = so + PS;  // the operand slot whose operand is read here
+      f += (rd < NA || rd >= NOP) ? 40 : 8;
+      if (so < NA && so % 2 == 1 && so / 2 < NC) f += 18;
+    }
     fixed[sl] = f;
     total += f;
   }
@@ -555,8 +563,8 @@ constexpr DqOpSched make_dq_op_sched() {
   t.first[NSL] = n;
   return t;
 }
-template <int PS, int NC, int NA, int NSL>
-constexpr DqOpSched kDqOps = make_dq_op_sched<PS, NC, NA, NSL>();
+template <int PS, int NC, int NA, int NOP, int NQB>
+constexpr DqOpSched kDqOps = make_dq_op_sched<PS, NC, NA, NOP, NQB>();
 
 template <bool BF16, int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
@@ -564,14 +572,17 @@ __attribute__((amdgpu_waves_per_eu(kBwdWavesQ<D>, kBwdWavesQ<D>)))
 fa_bwd_dq_wide_kernel(const BwdParams p) {
   using E = Elt<BF16>;
   constexpr int CPR = D / 8, NDS = D / 16, NDB = D / 32, NW = 4, KB = 32, R = 6, AHEAD = 5;
+  constexpr int NQB = kDqBlocks<D>;
+  constexpr int QW = NW * 32 * NQB;  // queries per workgroup
   constexpr int SLOT = KB * CPR;  // 16-byte chunks of one block's K (or V) rows
   constexpr int PPW = SLOT / 64 / NW;  // 1 KB pieces per wave, block and tensor
   constexpr int NC = 2 * PPW;     // copies per wave and block: K, then V
-  constexpr int NA = 2 * NDB;     // dQ slots per iteration (then NDS x (S, dP))
-  constexpr int NSL = NA + 2 * NDS;
+  constexpr int NA = 2 * NDB;     // dQ operand slots per iteration (then NDS x (K, V))
+  constexpr int NOP = NA + 2 * NDS;
   constexpr int PS = FA_BQ_PS < NA ? FA_BQ_PS : NA;
   static_assert(D == 64 || D == 128, "head dims");
-  static_assert(NC <= NA / 2 + NA % 2 && NSL % 2 == 0, "copies fit the dQ slots");
+  static_assert(NQB == 1 || NQB == 2, "one or two query blocks per wave");
+  static_assert(NC <= NA / 2 && NOP % 2 == 0, "copies fit the dQ slots");
   static_assert(PS >= 2 && 2 * PS <= 15 && PS % 2 == 0,
                 "operands read a few (even) slots ahead (lgkmcnt holds 15)");
   static_assert(R % 2 == 0 && R >= AHEAD + 1, "ring: even and deep enough");
@@ -581,39 +592,55 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
-  const int n_qt = (N + 127) / 128;
+  const int n_qt = (N + QW - 1) / QW;
   int bh, rank;
   tile_order<CAUSAL>(blockIdx.x, p.BH, n_qt, bh, rank);
   const int qt = CAUSAL ? n_qt - 1 - rank : rank;  // the last query tile sees the most keys
   const size_t head = (size_t)bh * (size_t)N * D;
-  const int q0 = qt * 128, wq0 = q0 + 32 * wid, qi = wq0 + l32;
-  const int qr = min(qi, N - 1);  // rows past N load row N-1 and are never stored
-  const int nb = CAUSAL ? (min(q0 + 128, N) + KB - 1) / KB : (N + KB - 1) / KB;
+  const int q0 = qt * QW;
+  // wave w owns query block w (and 2 NW - 1 - w with two per wave), so that under the
+  // causal mask the waves of a workgroup end within a key block of each other
+  int qbase[NQB], qi[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    qbase[qb] = q0 + 32 * (qb == 0 ? wid : 2 * NW - 1 - wid);
+    qi[qb] = qbase[qb] + l32;
+  }
+  const int nb = CAUSAL ? (min(q0 + QW, N) + KB - 1) / KB : (N + KB - 1) / KB;
   const float c = p.c;
   const float s_mask = c > 0.f ? -__builtin_inff() : __builtin_inff();
 
-  // Q and dO as B operands (lane: query qr, columns 16 ds + 8 hh ..), in AGPRs; D_i from
-  // dO and O; L_i log2(e)
-  u32x4_t qf[NDS], dof[NDS];
-  float dpart = 0.f;
+  // Q and dO as B operands (lane: query, columns 16 ds + 8 hh ..), in AGPRs; D_i from dO
+  // and O; L_i log2(e); rows past N load row N - 1 and are never stored
+  u32x4_t qf[NQB][NDS], dof[NQB][NDS];
+  float Dq[NQB], L2[NQB];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    const size_t off = head + (size_t)qr * D + ds * 16 + hh * 8;
-    qf[ds] = ld16(p.q + off);
-    dof[ds] = ld16(p.dout + off);
-    const u32x4_t of = ld16(p.o + off);
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qr = min(qi[qb], N - 1);
+    float dpart = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) dpart = E::dot2(dof[ds][w], of[w], dpart);
+    for (int ds = 0; ds < NDS; ++ds) {
+      const size_t off = head + (size_t)qr * D + ds * 16 + hh * 8;
+      qf[qb][ds] = ld16(p.q + off);
+      dof[qb][ds] = ld16(p.dout + off);
+      const u32x4_t of = ld16(p.o + off);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dpart = E::dot2(dof[qb][ds][w], of[w], dpart);
+    }
+    Dq[qb] = xhalf_sum(dpart);
+    L2[qb] = p.lse[(size_t)bh * N + qr] * 1.4426950408889634f;
   }
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+a"(qf[ds]), "+a"(dof[ds]));
-  const float Dq = xhalf_sum(dpart);
-  const float L2 = p.lse[(size_t)bh * N + qr] * 1.4426950408889634f;
-  f32x16_t dq[D / 32];  // dQ^T: rows = head dims, lane = query; in AGPRs
+  for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int ds = 0; ds < NDS; ++ds) asm volatile("" : "+a"(qf[qb][ds]), "+a"(dof[qb][ds]));
+  f32x16_t dq[NQB][NDB];  // dQ^T: rows = head dims, lane = query; in AGPRs
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+  for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[qb][db][r] = 0.f;
 
   // ---- copies: block g (keys 32 g ..) into ring slot sl: copies 0 .. PPW - 1 move 1 KB
   // pieces wid, wid + 4, .. of the K rows, the next PPW those of the V rows (lane l of
@@ -658,9 +685,9 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
       asm volatile("" : "+v"(taddr[db][h]));
     }
   typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
-  // the A operand of slot s of an iteration: s < NA, dQ step s (16-key half s / NDB,
-  // head dims 32 (s % NDB) ..) from K^T of slot slt; s >= NA, the K (even) or V (odd)
-  // rows of head-dim step (s - NA) / 2 of slot slr
+  // the A operand of operand slot s of an iteration: s < NA, dQ step s (16-key half
+  // s / NDB, head dims 32 (s % NDB) ..) from K^T of slot slt; s >= NA, the K (even) or V
+  // (odd) rows of head-dim step (s - NA) / 2 of slot slr
   auto operand = [&](int s, int slt, int slr) __attribute__((always_inline)) {
     if (s < NA) {
       const uint32_t off = (uint32_t)(slt * SLOT * 16 + (s / NDB) * 16 * CPR * 16);
@@ -675,21 +702,23 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
     return *(lds_u32x4_t*)(uintptr_t)(raddr[w][ds] + (uint32_t)(slr * SLOT * 16));
   };
 
-  // ---- the softmax terms of one block ---------------------------------------------------
-  constexpr DqOpSched OPS = kDqOps<PS, NC, NA, NSL>;
+  // ---- the softmax terms of one key block ------------------------------------------------
+  typedef f32x16_t Tiles[NQB];
+  typedef u32x4_t DsOps[NQB][2];
+  constexpr DqOpSched OPS = kDqOps<PS, NC, NA, NOP, NQB>;
   float xq[2][2], dq3[3][2], pq[2][2], eq[2][2];
-  auto soft_op = [&](const f32x16_t& s, const f32x16_t& dp, u32x4_t (&dsop)[2], int o)
+  auto soft_op = [&](const Tiles& s, const Tiles& dp, DsOps& dsop, int o)
       __attribute__((always_inline)) {
     const int v = OPS.code[o] / 10, op = OPS.code[o] % 10;
-    const int r0 = 2 * v;
+    const int qb = v / 8, r0 = 2 * (v % 8);
     if (op < 2) {
-      xq[v % 2][op] = __builtin_fmaf(s[r0 + op], c, -L2);
+      xq[v % 2][op] = __builtin_fmaf(s[qb][r0 + op], c, -L2[qb]);
       asm volatile("" : "+v"(xq[v % 2][op]));
     } else if (op < 4) {
       pq[v % 2][op - 2] = __builtin_amdgcn_exp2f(xq[v % 2][op - 2]);
       asm volatile("" : "+v"(pq[v % 2][op - 2]));
     } else if (op < 6) {
-      dq3[v % 3][op - 4] = dp[r0 + op - 4] - Dq;
+      dq3[v % 3][op - 4] = dp[qb][r0 + op - 4] - Dq[qb];
       asm volatile("" : "+v"(dq3[v % 3][op - 4]));
     } else if (op < 8) {
       eq[v % 2][op - 6] = pq[v % 2][op - 6] * dq3[v % 3][op - 6];
@@ -697,64 +726,76 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
     } else {
       uint32_t w = E::pack(eq[v % 2][0], eq[v % 2][1]);
       asm volatile("" : "+v"(w));
-      dsop[r0 / 8][(r0 % 8) / 2] = w;
+      dsop[qb][r0 / 8][(r0 % 8) / 2] = w;
     }
   };
-  // causal: register r (key 32 g + 8 hh + key_of_reg(r, 0)) keeps when that key <= qi;
-  // only blocks that reach past the wave's first query need it
-  auto mask = [&](f32x16_t& s, int g) __attribute__((always_inline)) {
-    if (!CAUSAL || g * KB + KB - 1 <= wq0) return;
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-    const int t = qi - (g * KB + 8 * hh);
+  // causal: register r (key 32 g + 8 hh + key_of_reg(r, 0)) keeps when that key <= the
+  // lane's query; only blocks that reach past the query block's first query need it
+  auto mask = [&](Tiles& s, int g) __attribute__((always_inline)) {
+    if (!CAUSAL) return;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[r];
-      asm("v_cmp_le_i32 vcc, %2, %1\n\tv_cndmask_b32 %0, %3, %0, vcc"
-          : "+v"(x) : "v"(t), "n"(key_of_reg(r, 0)), "v"(s_mask) : "vcc");
-      s[r] = x;
+    for (int qb = 0; qb < NQB; ++qb) {
+      if (g * KB + KB - 1 <= qbase[qb]) continue;
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[qb]));
+      const int t = qi[qb] - (g * KB + 8 * hh);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[qb][r];
+        asm("v_cmp_le_i32 vcc, %2, %1\n\tv_cndmask_b32 %0, %3, %0, vcc"
+            : "+v"(x) : "v"(t), "n"(key_of_reg(r, 0)), "v"(s_mask) : "vcc");
+        s[qb][r] = x;
+      }
     }
   };
-  auto zero16 = [](f32x16_t& x) {
+  auto zero = [](Tiles& x) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[qb][r] = 0.f;
   };
 
   // ---- one iteration: dQ of block t; softmax terms of block t+1; S, dP of block t+2 ----
-  u32x4_t onext[PS];  // operands of the next iteration's first PS slots
-  auto iteration = [&](int u, int t, f32x16_t& s_new, f32x16_t& dp_new, const f32x16_t& s_mid,
-                       const f32x16_t& dp_mid, u32x4_t (&ds_mid)[2], const u32x4_t (&ds_cur)[2])
+  u32x4_t onext[PS];  // operands of the next iteration's first PS operand slots
+  auto iteration = [&](int u, int t, Tiles& s_new, Tiles& dp_new, const Tiles& s_mid,
+                       const Tiles& dp_mid, DsOps& ds_mid, const DsOps& ds_cur)
       __attribute__((always_inline)) {
     const int sl0 = u, sl1 = (u + 1) % R, sl2 = (u + 2) % R, slc = (u + AHEAD) % R;
-    u32x4_t opd[NSL];
+    u32x4_t opd[NOP];
 #pragma unroll
     for (int s = 0; s < PS; ++s) opd[s] = onext[s];
-    zero16(s_new);
-    zero16(dp_new);
+    zero(s_new);
+    zero(dp_new);
 #pragma unroll
-    for (int s = 0; s < NSL; ++s) {
-      // one LDS wait per two slots: the operands of slots s and s + 1 together
-      if (s % 2 == 0) {
+    for (int sl = 0; sl < NOP * NQB; ++sl) {
+      const int s = sl / NQB, qb = sl % NQB;
+      // one LDS wait per two operand slots: the operands of s and s + 1 together
+      if (qb == 0 && s % 2 == 0) {
         asm volatile("" ::"v"(opd[s]), "v"(opd[s + 1]));
         __builtin_amdgcn_sched_barrier(0);
       }
       if (s < NA) {
-        // keep the previous step's sources live until this step (the inline-assembly
+        // keep the previous product's sources live until this one (the inline-assembly
         // MFMAs read them over several cycles)
-        if (s > 0) asm volatile("" ::"v"(opd[s - 1]), "v"(ds_cur[(s - 1) / NDB]));
-        mfma_acc_agpr<BF16>(dq[s % NDB], opd[s], ds_cur[s / NDB]);
+        if (sl > 0) {
+          const int ps = (sl - 1) / NQB, pq2 = (sl - 1) % NQB;
+          asm volatile("" ::"v"(opd[ps]), "v"(ds_cur[pq2][ps / NDB]));
+        }
+        mfma_acc_agpr<BF16>(dq[qb][s % NDB], opd[s], ds_cur[qb][s / NDB]);
       } else if ((s - NA) % 2 == 0) {
-        s_new = E::mfma(opd[s], qf[(s - NA) / 2], s_new);
+        s_new[qb] = E::mfma(opd[s], qf[qb][(s - NA) / 2], s_new[qb]);
       } else {
-        dp_new = E::mfma(opd[s], dof[(s - NA) / 2], dp_new);
+        dp_new[qb] = E::mfma(opd[s], dof[qb][(s - NA) / 2], dp_new[qb]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (s + PS < NSL) opd[s + PS] = operand(s + PS, sl0, sl2);
-      else onext[s + PS - NSL] = operand(s + PS - NSL, sl1, sl1);
-      if (s < NA && s % 2 == 1 && s / 2 < NC) copy(t + AHEAD, slc, s / 2);
+      if (qb == 0) {
+        if (s + PS < NOP) opd[s + PS] = operand(s + PS, sl0, sl2);
+        else onext[s + PS - NOP] = operand(s + PS - NOP, sl1, sl1);
+        if (s < NA && s % 2 == 1 && s / 2 < NC) copy(t + AHEAD, slc, s / 2);
+      }
 #pragma unroll
-      for (int o = OPS.first[s]; o < OPS.first[s + 1]; ++o) soft_op(s_mid, dp_mid, ds_mid, o);
+      for (int o = OPS.first[sl]; o < OPS.first[sl + 1]; ++o) soft_op(s_mid, dp_mid, ds_mid, o);
       __builtin_amdgcn_sched_barrier(0);
-      if (s == NA - 1) asm volatile("" ::"v"(opd[NA - 1]), "v"(ds_cur[1]));
+      if (sl == NA * NQB - 1) asm volatile("" ::"v"(opd[NA - 1]), "v"(ds_cur[NQB - 1][1]));
     }
     mask(s_new, t + 2);
   };
@@ -767,22 +808,30 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
     for (int cc = 0; cc < NC; ++cc) copy(b, b, cc);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"((AHEAD - 2) * NC) : "memory");  // blocks 0, 1
   __syncthreads();
-  f32x16_t sA, sB, dA, dB;
-  u32x4_t dsA[2], dsB[2];
-  zero16(sA);
-  zero16(dA);
-  zero16(sB);
-  zero16(dB);
+  Tiles sA, sB, dA, dB;
+  DsOps dsA, dsB;
+  zero(sA);
+  zero(dA);
+  zero(sB);
+  zero(dB);
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) {
-    sA = E::mfma(operand(NA + 2 * ds, 0, 0), qf[ds], sA);
-    dA = E::mfma(operand(NA + 1 + 2 * ds, 0, 0), dof[ds], dA);
+    const u32x4_t ka = operand(NA + 2 * ds, 0, 0), va = operand(NA + 1 + 2 * ds, 0, 0);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      sA[qb] = E::mfma(ka, qf[qb][ds], sA[qb]);
+      dA[qb] = E::mfma(va, dof[qb][ds], dA[qb]);
+    }
   }
   mask(sA, 0);
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) {
-    sB = E::mfma(operand(NA + 2 * ds, 0, 1), qf[ds], sB);
-    dB = E::mfma(operand(NA + 1 + 2 * ds, 0, 1), dof[ds], dB);
+    const u32x4_t kb = operand(NA + 2 * ds, 0, 1), vb = operand(NA + 1 + 2 * ds, 0, 1);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      sB[qb] = E::mfma(kb, qf[qb][ds], sB[qb]);
+      dB[qb] = E::mfma(vb, dof[qb][ds], dB[qb]);
+    }
   }
 #pragma unroll
   for (int o = 0; o < OPS.n; ++o) soft_op(sA, dA, dsA, o);
@@ -810,8 +859,12 @@ fa_bwd_dq_wide_kernel(const BwdParams p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dq[db]));
-  if (qi < N) bwd_store_rows<BF16, D>(p.dq + head, dq, qi, hh, p.scale);
+  for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dq[qb][db]));
+    if (qi[qb] < N) bwd_store_rows<BF16, D>(p.dq + head, dq[qb], qi[qb], hh, p.scale);
+  }
 }
 
 }  // namespace fa
