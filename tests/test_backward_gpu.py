@@ -125,6 +125,24 @@ def test_backward_scale_values(scale, d):
         _case(Workload("scale", 1, 2, 200, d, "bf16", causal, seed=7900 + d), scale=scale)
 
 
+# Grids of several workgroups per CU with B*H not a multiple of 8 (the non-XCD tile
+# order), ragged N at both head dims, and fp16 at d = 128 under the causal mask: every
+# element against the oracle.
+GRIDS = [
+    # name, B, H, N, d, dtype, causal
+    ("bh15_causal", 3, 5, 1100, 128, "bf16", True),
+    ("bh15", 3, 5, 1100, 128, "bf16", False),
+    ("bh7_d64_causal", 1, 7, 2047, 64, "fp16", True),
+    ("bh6_fp16_causal", 2, 3, 1500, 128, "fp16", True),
+]
+
+
+@pytest.mark.parametrize("case", GRIDS, ids=[c[0] for c in GRIDS])
+def test_backward_grid_shapes(case):
+    name, B, H, N, d, dt, causal = case
+    _case(Workload(name, B, H, N, d, dt, causal, seed=8100 + N + d))
+
+
 # ------------------------------------------------------ full-size workloads, sampled heads
 @pytest.mark.parametrize("name", ["ai2048", "causal8k", "stress4000"])
 def test_backward_full_workload_sampled_heads(name):
