@@ -26,6 +26,9 @@ WARMUP_MIN_S = 0.3          # least back-to-back warmup before the timed steps (
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 matrix peak, published
 CSRC = os.path.join(ROOT, "io_aware_exact_fa2_amd", "csrc")
+# Shapes with too few query tiles to fill the GPU, timed through fa_fwd and through
+# fa_fwd_splitkv with this many key splits
+SPLITKV = {"few16k": 4, "fewc16k": 3}
 
 
 def kernel_hash() -> str:
@@ -279,6 +282,13 @@ def _is_kernel(name, path):
     return "fa_fwd" in name and "fa1" not in name and "fp8" not in name
 
 
+def _is_split(name):
+    """The two kernels of the split-KV pass: the forward's split instantiation (its last
+    template argument) and the merge."""
+    return "fa_split_merge" in name or ("fa_fwd_fast_kernel" in name and
+                                        name.split(">(")[0].endswith("true"))
+
+
 def _kernel_stats(directory, path):
     """(name, calls, average ns, min ns, max ns) of the kernel, from --stats output."""
     rows = _csv_rows(directory, "kernel_stats.csv")
@@ -454,10 +464,12 @@ def summarize_traces(path, entries, sq_dirs=None, hbm_dirs=None, copy_mib=512,
 
     out_dir = out_dir or os.path.join(ROOT, "profiles")
     pred = {"bwd": lambda n: "fa_bwd" in n, "fp8": lambda n: "fa_fwd_fp8" in n,
-            "fa1": lambda n: "fa_fwd_fa1" in n}[path]
+            "fa1": lambda n: "fa_fwd_fa1" in n,
+            "splitkv": lambda n: _is_split(n) or _is_kernel(n, "fwd")}[path]
     factor = 2.5 if path == "bwd" else 1.0
     title = {"bwd": "fa_bwd backward kernels", "fp8": "fa_fwd_fp8 (E4M3 forward)",
-             "fa1": "fa_fwd_fa1 (the FA1 loop order)"}[path]
+             "fa1": "fa_fwd_fa1 (the FA1 loop order)",
+             "splitkv": "fa_fwd_splitkv (keys split across workgroups) against fa_fwd"}[path]
     rec = {"path": path, "kernel_source_sha256_16": kernel_hash(), "workloads": {}}
     lines = [f"# {title} — rocprofv3 summary", "",
              f"Kernel source hash (bench.py `kernel_hash`): {rec['kernel_source_sha256_16']}. "
@@ -481,15 +493,27 @@ def summarize_traces(path, entries, sq_dirs=None, hbm_dirs=None, copy_mib=512,
     for wl, kt_dir in entries:
         w = workloads.get(wl)
         ks = _all_kernel_stats(kt_dir, pred)
-        total = sum(k[2] for k in ks)
+        if path == "splitkv":
+            # the split pass is its partial kernel plus the merge; fa_fwd is one kernel
+            total = sum(k[2] for k in ks if _is_split(k[0]))
+            plain = sum(k[2] for k in ks if not _is_split(k[0]))
+        else:
+            total = sum(k[2] for k in ks)
         tf = factor * w.flops() / (total * 1e-9) / 1e12 if total else 0.0
         rec["workloads"][wl] = {"kernels": {k[0]: {"calls": k[1], "average_ns": k[2],
                                                    "min_ns": k[3], "max_ns": k[4]} for k in ks},
                                 "sum_of_averages_ns": total, "tflops": tf}
+        if path == "splitkv":
+            rec["workloads"][wl].update({
+                "splits": SPLITKV.get(wl, 4), "fa_fwd_ns": plain,
+                "fa_fwd_tflops": w.flops() / (plain * 1e-9) / 1e12 if plain else 0.0,
+                "speedup": plain / total if total else 0.0})
         for k in ks:
             row = f"| {wl} | {_shape(w, path)} | `{k[0]}` | {k[1]} | {k[2] / 1e3:.1f} | " \
                   f"{k[3] / 1e3:.1f} | {k[4] / 1e3:.1f} |"
-            if path != "bwd":
+            if "fa_split_merge" in k[0]:
+                row += " (merge) |"
+            elif path != "bwd":
                 row += f" {w.flops() / (k[2] * 1e-9) / 1e12:.1f} |"
             lines.append(row)
         summary.append((wl, total, tf))
@@ -499,6 +523,17 @@ def summarize_traces(path, entries, sq_dirs=None, hbm_dirs=None, copy_mib=512,
                   "% of 2500 |", "|---|---|---|---|"]
         lines += [f"| {wl} | {t / 1e3:.1f} | {tf:.1f} | {100 * tf / 2500:.1f} |"
                   for wl, t, tf in summary]
+        lines.append("")
+    elif path == "splitkv":
+        lines += ["Split-KV time = the partial kernel's average + the merge kernel's average "
+                  "(one call runs both); fa_fwd time = its one kernel's average, same shape.", "",
+                  "| workload | splits | fa_fwd µs | TFLOPS | split-KV µs | TFLOPS | speedup |",
+                  "|---|---|---|---|---|---|---|"]
+        for wl, t, tf in summary:
+            r = rec["workloads"][wl]
+            lines.append(f"| {wl} | {r['splits']} | {r['fa_fwd_ns'] / 1e3:.1f} | "
+                         f"{r['fa_fwd_tflops']:.1f} | {t / 1e3:.1f} | {tf:.1f} | "
+                         f"{r['speedup']:.2f} |")
         lines.append("")
     elif path == "fp8":
         lines += ["Against the 5000 TFLOPS dense FP8 peak: " + ", ".join(
@@ -672,11 +707,15 @@ def main(argv=None):
                     help="extra workloads timed for the 'workloads' field ('' for none)")
     ap.add_argument("--path", default="fwd",
                     help="with --summarize-hbm or for profiling runs: fwd (the FA2-order "
-                         "forward, the default and the headline), bwd, fa1, splitkvS")
+                         "forward, the default and the headline), bwd, fp8, fa1, splitkvS "
+                         "(S key splits), splitkv (fa_fwd, then the split-KV pass)")
     ap.add_argument("--backward", default="ai2048,causal8k,long32k,stress4000",
                     help="workloads whose backward pass is also timed (comma list; empty: none)")
     ap.add_argument("--fp8", default="ai2048,causal8k,long32k",
                     help="workloads whose 8-bit (E4M3) forward is also timed (empty: none)")
+    ap.add_argument("--splitkv", default=",".join(f"{k}:{v}" for k, v in SPLITKV.items()),
+                    help="few-tile workloads timed through fa_fwd and fa_fwd_splitkv "
+                         "(name:splits comma list; empty: none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-hbm", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -692,7 +731,7 @@ def main(argv=None):
     ap.add_argument("--sq-dirs", nargs=2, metavar=("SQ1_DIR", "SQ2_DIR"))
     ap.add_argument("--hbm-dirs", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-args", default=" --cpu-budget 0 --also '' --backward '' "
-                    "--fp8 '' --steps 20 --warmup 3",
+                    "--fp8 '' --splitkv '' --steps 20 --warmup 3",
                     help="bench.py arguments the profiled runs used (recorded)")
     a = ap.parse_args(argv)
     if a.summarize_traces:
@@ -729,6 +768,14 @@ def main(argv=None):
     if a.calibrate_copy_mib:
         calibrate_copy(a.calibrate_copy_mib)
     w = workloads.get(a.workload)
+    if a.path == "splitkv":
+        # the plain forward, then the split-KV pass, on one shape (for profiling runs)
+        for leg in ("fwd", f"splitkv{SPLITKV.get(w.name, 4)}"):
+            msx, _, ranx = time_gpu(w, a.steps, a.warmup, leg=leg)
+            print(json.dumps({"path": leg, "workload": w.name, "ms": round(msx, 5),
+                              "tflops": round(w.flops() / (msx * 1e-3) / 1e12, 2),
+                              "steps": a.steps, "warmup_steps_run": ranx}), flush=True)
+        return 0
     if a.path != "fwd":
         # one pass other than the headline forward, for profiling runs
         msx, wallx, ranx = time_gpu(w, a.steps, a.warmup, leg=a.path)
@@ -785,6 +832,19 @@ def main(argv=None):
                     "pct_fp8_peak": round(100 * tx / PEAK_FP8_TFLOPS, 1),
                     "causal": wx.causal, "shape": [wx.B, wx.H, wx.N, wx.d],
                     "inputs": "E4M3 codes with per-tensor scales, bf16 O"}
+    skv = {}
+    for item in [s for s in a.splitkv.split(",") if s]:
+        name, _, ns = item.partition(":")
+        wx = workloads.get(name)
+        ns = int(ns or SPLITKV.get(name, 4))
+        ms_f, _, _ = time_gpu(wx, max(5, a.steps // 5), 3)
+        ms_s, _, _ = time_gpu(wx, max(5, a.steps // 5), 3, leg=f"splitkv{ns}")
+        skv[name] = {"shape": [wx.B, wx.H, wx.N, wx.d], "causal": wx.causal, "dtype": wx.dtype,
+                     "splits": ns, "fa_fwd_ms": round(ms_f, 4),
+                     "fa_fwd_tflops": round(wx.flops() / (ms_f * 1e-3) / 1e12, 1),
+                     "splitkv_ms": round(ms_s, 4),
+                     "splitkv_tflops": round(wx.flops() / (ms_s * 1e-3) / 1e12, 1),
+                     "speedup": round(ms_f / ms_s, 3)}
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -814,6 +874,7 @@ def main(argv=None):
         "workloads": extra,
         "backward": bwd,
         "fp8": f8,
+        "splitkv": skv,
     }
     if a.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_budget)

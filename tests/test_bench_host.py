@@ -121,3 +121,32 @@ def test_trace_summary_backward(tmp_path):
     assert sq["waitcnt_pct_of_wave_cycles"] == pytest.approx(30.0)
     md = (out / "fa_bwd_rocprof.md").read_text()
     assert "--summarize-traces ai2048=<kt_dir_ai2048>" in md and names[2] in md
+
+
+def test_trace_summary_splitkv(tmp_path):
+    """The split-KV summary adds the partial kernel and the merge into one pass and sets it
+    against the plain forward's one kernel on the same shape."""
+    w = workloads.get("few16k")
+    fwd = "void fa::fa_fwd_wide_kernel<true, 128, false, 64, 4>(fa::Params)"
+    part = "void fa::fa_fwd_fast_kernel<true, 128, false, 4, 64, 2, true>(fa::Params)"
+    merge = "void fa::fa_split_merge_kernel<true, 128>(float const*, float const*, " \
+            "unsigned short*, float*, long long, int)"
+    kt = str(tmp_path / "kt")
+    _write(os.path.join(kt, "host", "kt_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+            "StdDev"],
+           [[COPY, 1, 5, 5, 0, 5, 5, 0], [fwd, 10, 4e6, 400_000.0, 60, 4e5, 4e5, 0],
+            [part, 10, 15e5, 150_000.0, 30, 1.5e5, 1.5e5, 0],
+            [merge, 10, 1e5, 10_000.0, 10, 1e4, 1e4, 0]])
+    out = tmp_path / "out"
+    out.mkdir()
+    rec = bench.summarize_traces("splitkv", [("few16k", kt)], out_dir=str(out))
+    r = rec["workloads"]["few16k"]
+    assert r["sum_of_averages_ns"] == pytest.approx(160_000.0)
+    assert r["fa_fwd_ns"] == pytest.approx(400_000.0)
+    assert r["speedup"] == pytest.approx(2.5)
+    assert r["tflops"] == pytest.approx(w.flops() / 160e-6 / 1e12)
+    assert r["fa_fwd_tflops"] == pytest.approx(w.flops() / 400e-6 / 1e12)
+    assert r["splits"] == bench.SPLITKV["few16k"]
+    md = (out / "fa_splitkv_rocprof.md").read_text()
+    assert "| few16k | 4 | 400.0 |" in md and "(merge)" in md

@@ -111,6 +111,26 @@ def test_variant_full_ai2048_sampled(path):
     _check(f"{path}/ai2048/sampled", "bf16", og, lg, O, L)
 
 
+@pytest.mark.parametrize("name", ["few16k", "fewc16k"])
+def test_splitkv_full_few_tile_every_row(name):
+    """Every row of the full few-tile shapes that the split-KV pass is for (64 or 128
+    query tiles for 256 compute units), through fa_fwd_splitkv with the split count the
+    benchmark times and through fa_fwd, against the float64 oracle."""
+    import bench
+
+    w = workloads.get(name)
+    q, k, v = workloads.make_inputs(w)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    O, L = oracle.attention(to_f64(q), to_f64(k), to_f64(v), w.scale, w.causal)
+    o, lse = fa.forward_splitkv(qd, kd, vd, causal=w.causal, scale=w.scale,
+                                n_splits=bench.SPLITKV[name])
+    torch.cuda.synchronize()
+    _check(f"splitkv/{name}/every_row", "bf16", o, lse, O, L)
+    o, lse = fa.forward(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    _check(f"fwd/{name}/every_row", "bf16", o, lse, O, L)
+
+
 def test_variants_agree_with_fa2():
     """The three loop organisations give the same O and L up to rounding on one input."""
     w = Workload("agree", 2, 4, 900, 128, "bf16", True, seed=8300)

@@ -24,6 +24,11 @@ Workloads (shapes are [B, H, N, d], row-major, contiguous):
                 round(1% of N) key rows get a spike of 8*sqrt(d)*u added, each
                 with its own direction u = g/|g|, g ~ N(0, I_d); V ~ U(-1, 1).
                 N is not a multiple of any tile size.
+* ``few16k``    1,1,16384,128 bf16, N(0,1), non-causal: one long head, whose 64
+                query tiles of 256 rows leave most of the 256 compute units idle
+                (the shape the split-KV pass is for)
+* ``fewc16k``   1,2,16384,128 bf16, N(0,1), causal: the same with two heads and
+                the causal mask
 
 Draw order inside one call: Q, K, V, then the spike row indices (one
 ``choice`` per head, heads in (b, h) order), then the spike directions. The
@@ -80,6 +85,8 @@ WORKLOADS = {
     "causal8k": Workload("causal8k", 2, 16, 8192, 128, "bf16", True, 3),
     "long32k": Workload("long32k", 1, 8, 32768, 128, "bf16", True, 4),
     "stress4000": Workload("stress4000", 8, 32, 4000, 64, "fp16", False, 5, "stress"),
+    "few16k": Workload("few16k", 1, 1, 16384, 128, "bf16", False, 6),
+    "fewc16k": Workload("fewc16k", 1, 2, 16384, 128, "bf16", True, 7),
 }
 
 
