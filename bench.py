@@ -639,7 +639,8 @@ def profile_record(workload: str, path: str = "fwd"):
 
 def profile_fields(workload: str, ms: float):
     """Per-config figures from the committed profile (HBM bytes and their rate at this
-    run's time, MFMA busy, LDS bank conflicts, clock under load), or a null marker."""
+    run's time, MFMA busy, VALU busy, LDS bank conflicts, clock under load), or a null
+    marker."""
     rec = profile_record(workload)
     if rec is None:
         return {"profile": None}
@@ -652,6 +653,8 @@ def profile_fields(workload: str, ms: float):
                     "lds_bank_conflict_cycles": sq["lds_bank_conflict_cycles"],
                     "valu_insts_per_mfma": round(sq["valu_insts_per_mfma"], 2),
                     "clock_GHz_under_load": round(sq["clock_GHz_under_load"], 3)})
+        if "valu_issue_pct_of_wave_cycles" in sq:
+            out["valu_busy_pct_of_wave_cycles"] = round(sq["valu_issue_pct_of_wave_cycles"], 1)
     out["profile"] = f"profiles/fa_fwd_{workload}_rocprof.md"
     return out
 
