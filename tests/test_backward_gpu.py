@@ -161,6 +161,29 @@ def test_backward_full_workload_sampled_heads(name):
     torch.cuda.empty_cache()
 
 
+def test_backward_full_ai2048_every_head():
+    """The full B=4, H=16, N=2048, d=128 shape in the launch the benchmark times: every
+    element of every head against the float64 oracle, each head held to the bar of the
+    reduced cases on its own."""
+    w = workloads.get("ai2048")
+    q, k, v = workloads.make_inputs(w)
+    do = workloads.make_grad(w)
+    got = [to_f64(t) for t in _gpu_grads(q, k, v, do, w.causal, w.scale)]
+    ref = oracle.attention_backward(to_f64(q), to_f64(k), to_f64(v), to_f64(do), w.scale,
+                                    w.causal)
+    rec = {"case": "ai2048/every_head", "dtype": w.dtype}
+    for tag, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.isfinite(g).all(), tag
+        err = np.abs(g - r).max(axis=(2, 3))
+        mx = np.abs(r).max(axis=(2, 3))
+        rec[f"worst_head_rel_max_{tag}"] = float((err / mx).max())
+    _REPORT.append(rec)
+    print(json.dumps(rec), flush=True)
+    assert all(rec[f"worst_head_rel_max_{t}"] <= TOL_G[w.dtype] for t in ("dQ", "dK", "dV")), rec
+    del got, ref
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["ai2048", "causal8k", "long32k", "stress4000"])
 def test_backward_constant_keys(name):
     """Identical key rows make each softmax row uniform over its allowed keys, so

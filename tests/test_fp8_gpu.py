@@ -172,6 +172,33 @@ def test_fp8_full_ai2048_sampled():
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
 
 
+@pytest.mark.parametrize("name", ["causal8k", "long32k"])
+def test_fp8_full_causal_sampled(name):
+    """The full causal shapes in one launch (the benchmark's 8-bit configurations):
+    sampled rows of the first and last head, at tile edges and near the end."""
+    w = workloads.get(name)
+    q8, k8, v8, qs, ks, vs = workloads.make_fp8_inputs(w)
+    o, lse = fa.forward_fp8(q8.to(DEV), k8.to(DEV), v8.to(DEV), qs, ks, vs, scale=w.scale,
+                            causal=True)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    rows = np.array([0, 1, 31, 32, 63, 64, 127, 128, 1000, w.N // 2 - 1, w.N // 2,
+                     w.N - 65, w.N - 64, w.N - 2, w.N - 1])
+    O, L = oracle.attention_fp8_rows(q8.numpy(), k8.numpy(), v8.numpy(), qs, ks, vs, w.scale,
+                                     True, heads, rows)
+    q, k, v = (oracle.decode_e4m3(t.numpy()) * s for t, s in ((q8, qs), (k8, ks), (v8, vs)))
+    parts = [_bounds(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                     w.scale, True, L[i][None, None], rows)
+             for i, (b, h) in enumerate(heads)]
+    bounds = tuple(np.stack([pt[j][0, 0] for pt in parts]) for j in range(3))
+    og = torch.stack([o[b, h, torch.as_tensor(rows)] for b, h in heads])
+    lg = torch.stack([lse[b, h, torch.as_tensor(rows)] for b, h in heads])
+    _check(f"fp8/{name}/sampled", og, lg, O, L, bounds)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    del o, lse
+    torch.cuda.empty_cache()
+
+
 def test_fp8_full_ai2048_every_row():
     """The full B=4, H=16, N=2048, d=128 shape in one launch: every row of every head
     against the oracle on the decoded inputs, under the bar above (the per-head bound
