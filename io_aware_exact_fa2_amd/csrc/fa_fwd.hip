@@ -148,7 +148,7 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
     // 64 queries per wave, one wave per SIMD
     e = cz ? launch_wide<BF16, 128, true>(p, s) : launch_wide<BF16, 128, false>(p, s);
   } else {
-    // 32 queries per wave, two waves per SIMD
+    // 32 queries per wave, two or three waves per SIMD (the register count decides)
     e = cz ? launch_fast<BF16, 64, true>(p, s) : launch_fast<BF16, 64, false>(p, s);
   }
   if (e != hipSuccess) {
