@@ -285,8 +285,9 @@ def _is_kernel(name, path):
 def _is_split(name):
     """The two kernels of the split-KV pass: the forward's split instantiation (its last
     template argument) and the merge."""
-    return "fa_split_merge" in name or ("fa_fwd_fast_kernel" in name and
-                                        name.split(">(")[0].endswith("true"))
+    return "fa_split_merge" in name or (
+        ("fa_fwd_fast_kernel" in name or "fa_fwd_wide_kernel" in name)
+        and name.split(">(")[0].endswith("true"))
 
 
 def _kernel_stats(directory, path):

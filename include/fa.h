@@ -179,9 +179,9 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float
  * of two).
  *
  * n_splits in [1, FA_MAX_SPLITS] is an upper bound: the keys per split are
- * ceil(N / n_splits) rounded up to a multiple of 128 (the query tile), so fewer splits
- * may run. Under
- * the causal mask a split that lies wholly after a query tile contributes L_s = -inf.
+ * ceil(N / n_splits) rounded up to a multiple of the query tile (256 rows at d = 128,
+ * 128 at d = 64), so fewer splits may run. Under the causal mask a split that lies
+ * wholly after a query tile contributes L_s = -inf.
  * d must be 64 or 128 (FA_ERR_UNSUPPORTED) and scale nonzero (FA_ERR_SHAPE).
  *
  * workspace: device memory of at least fa_fwd_splitkv_workspace_size(B, H, N, d,

@@ -159,23 +159,28 @@ int fa_fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse
 }
 
 // ---- split-KV and FA1-order passes (caller-provided workspace) --------------------
-constexpr int kSplitBR = kFNW * 32;  // query rows per split-KV workgroup (fast kernel)
 constexpr size_t kWsAlign = 256;
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Query rows per split-KV workgroup: the wide kernel's 256 at d = 128, the 32-query
+// kernel's 128 at d = 64.
+int split_tile(int d) {
+  return d == 128 ? fa::WideGeom<128, FA_WIDE_BC, FA_WIDE_RING>::BR : kFNW * 32;
+}
+
 // Effective split count and keys per split (a multiple of the query tile), or 0.
-int split_geometry(int N, int n_splits, int* keys_per_split) {
+int split_geometry(int N, int n_splits, int tile, int* keys_per_split) {
   if (N < 1 || n_splits < 1 || n_splits > FA_MAX_SPLITS) return 0;
   const int per = (N + n_splits - 1) / n_splits;
-  const int keys = (per + kSplitBR - 1) / kSplitBR * kSplitBR;
+  const int keys = (per + tile - 1) / tile * tile;
   if (keys_per_split) *keys_per_split = keys;
   return (N + keys - 1) / keys;
 }
 
 size_t splitkv_bytes(int B, int H, int N, int d, int n_splits) {
   if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
-  const int ns = split_geometry(N, n_splits, nullptr);
+  const int ns = split_geometry(N, n_splits, split_tile(d), nullptr);
   if (ns == 0) return 0;
   const uint64_t rows = static_cast<uint64_t>(B) * H * N;
   if (rows > (uint64_t(1) << 40)) return 0;
@@ -211,12 +216,17 @@ int validate_ws(const void* q, const void* k, const void* v, const void* o, cons
 
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_splitkv(fa::Params p, int n_eff, hipStream_t stream) {
-  constexpr int WPE = D == 128 ? FA_WPE_D128 : FA_WPE_D64;
-  constexpr int BC = D == 128 ? FA_BC_D128 : FA_BC_D64;
-  p.n_qt = (p.N + kSplitBR - 1) / kSplitBR;
+  const int tile = split_tile(D);
+  p.n_qt = (p.N + tile - 1) / tile;
   const int grid = p.n_qt * p.BH * n_eff;
-  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, BC, WPE, true>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
+  if constexpr (D == 128) {
+    using G = fa::WideGeom<D, FA_WIDE_BC, FA_WIDE_RING>;
+    auto kern = fa::fa_fwd_wide_kernel<BF16, D, CAUSAL, FA_WIDE_BC, FA_WIDE_RING, true>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(G::NW * 64), 0, stream, p);
+  } else {
+    auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, FA_BC_D64, FA_WPE_D64, true>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long rows = static_cast<long long>(p.BH) * p.N;
@@ -233,12 +243,13 @@ int fa_splitkv_impl(const void* q, const void* k, const void* v, void* o, float*
   int st = validate(q, k, v, o, lse, B, H, N, d, scale, 0.f);
   if (st != FA_OK) return st;
   int keys = 0;
-  const int n_eff = split_geometry(N, n_splits, &keys);
+  const int tile = split_tile(d);
+  const int n_eff = split_geometry(N, n_splits, tile, &keys);
   if (n_eff == 0) return FA_ERR_SHAPE;
   const size_t need = splitkv_bytes(B, H, N, d, n_splits);
   st = validate_ws(q, k, v, o, lse, ws, ws_bytes, need, B, H, N, d, scale);
   if (st != FA_OK) return st;
-  const int64_t grid = static_cast<int64_t>((N + kSplitBR - 1) / kSplitBR) * B * H * n_eff;
+  const int64_t grid = static_cast<int64_t>((N + tile - 1) / tile) * B * H * n_eff;
   if (grid >= (int64_t(1) << 31) / 64) return FA_ERR_SHAPE;
   fa::Params p;
   p.q = static_cast<const uint16_t*>(q);

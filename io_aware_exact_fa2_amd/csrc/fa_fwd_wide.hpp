@@ -7,7 +7,9 @@
 // query row block is the outer loop (one workgroup per query block, head and batch),
 // key/value blocks stream through LDS in the inner loop, each row keeps its running
 // max and sum on chip, rescales the unnormalised output by alpha = exp(m_old - m_new)
-// only, and divides once at the end. Waves own disjoint query rows (split-Q).
+// only, and divides once at the end. Waves own disjoint query rows (split-Q). With
+// SPLIT, workgroup (s, head, query block) covers only the keys of split s and writes its
+// normalized partial O and partial L in float32 for the split-KV merge (fa_fwd_split.hpp).
 //
 // Why this kernel. With one wave per SIMD the wave issues everything itself, and the
 // softmax's VALU work per tile (one FMA, one exponential, one add per score, half a
@@ -175,7 +177,7 @@ template <int NPAIR, int NSLOT, int LB, int LC, int SC_N, int NQK, int NPV, int 
 constexpr OpSched<NPAIR, NSLOT> kOpSched =
     make_op_sched<NPAIR, NSLOT, LB, LC, SC_N, NQK, NPV, PF, NDMA>();
 
-template <bool BF16, int D, bool CAUSAL, int BC, int R>
+template <bool BF16, int D, bool CAUSAL, int BC, int R, bool SPLIT = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_fwd_wide_kernel(const Params p) {
   using G = WideGeom<D, BC, R>;
@@ -186,6 +188,7 @@ fa_fwd_wide_kernel(const Params p) {
   constexpr int SC_N = 2 * NPV;                 // slots of the P V block (tile j)
   constexpr int NSLOT = SB_N + SC_N;
   constexpr int NPAIR = BC / 2;                 // score pairs per lane and tile
+  constexpr int PF = FA_W_PF;                   // MFMA steps an LDS operand read runs ahead
   static_assert(R >= 4 && R % 2 == 0, "the ring holds the tiles of three stages");
   __shared__ __attribute__((aligned(1024))) u32x4_t kbuf[R * CHUNKS];
   __shared__ __attribute__((aligned(1024))) u32x4_t vbuf[R * CHUNKS];
@@ -197,25 +200,43 @@ fa_fwd_wide_kernel(const Params p) {
   const int hh = lane >> 5;
   const int N = p.N;
 
-  int bh, qt;
-  decode_tile<CAUSAL>(p, blockIdx.x, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (SPLIT) {
+    // split-major grid: every split sees the same (head, tile) decode
+    const int per = p.n_qt * p.BH;
+    split = blockIdx.x / per;
+    decode_tile<CAUSAL>(p, blockIdx.x % per, bh, qt);
+  } else {
+    decode_tile<CAUSAL>(p, blockIdx.x, bh, qt);
+  }
+  // keys [kofs, kofs + Nk) of the head; key indices below are relative to kofs (the
+  // whole head unless this is a split-KV partial pass)
+  const int kofs = SPLIT ? split * p.split_keys : 0;
+  const int Nk = SPLIT ? min(N - kofs, p.split_keys) : N;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t* __restrict__ qg = p.q + head;
-  const uint16_t* __restrict__ kg = p.k + head;
-  const uint16_t* __restrict__ vg = p.v + head;
+  const uint16_t* __restrict__ kg = p.k + head + (size_t)kofs * D;
+  const uint16_t* __restrict__ vg = p.v + head + (size_t)kofs * D;
 
   const int q0 = qt * G::BR;
   // wave w owns the 32-query blocks w and 7 - w of the workgroup's 256 queries
   const int qbase[2] = {q0 + 32 * wid, q0 + 32 * (2 * NW - 1 - wid)};
   const int wq0 = qbase[0];
   const int q_end = min(q0 + G::BR, N);
-  const int n_kt = CAUSAL ? (q_end + BC - 1) / BC : (N + BC - 1) / BC;
+  const int n_kt = CAUSAL ? (min(q_end - kofs, Nk) + BC - 1) / BC : (Nk + BC - 1) / BC;
+  // Splits start at multiples of the query tile, so under the causal mask a split either
+  // starts at or before q0 (every query of the tile sees its first key) or after the
+  // tile's last query: empty (n_kt <= 0), partial L = -inf and partial O = 0. An empty
+  // split's workgroup runs the prologue on empty buffers (its copies read no memory), no
+  // iteration, and writes those values; an early return here, or a loop known to run
+  // at least once, would cost the loop registers.
+  const bool empty = SPLIT && n_kt <= 0;
   const bool wave_live = wq0 < N;
   const int w_last_q = min(qbase[1] + 32, N) - 1;
-  const int w_kt = CAUSAL ? min(n_kt, w_last_q / BC + 1) : n_kt;
-  // the first tile that reaches past N or, under the causal mask, past the wave's first
-  // query (key t BC + BC - 1 > wq0), and the number of the wave's tiles from there on
-  const int t_mask = CAUSAL ? min(N / BC, (wq0 + 1) / BC) : N / BC;
+  const int w_kt = empty ? 0 : CAUSAL ? min(n_kt, (w_last_q - kofs) / BC + 1) : n_kt;
+  // the first tile that reaches past the keys or, under the causal mask, past the wave's
+  // first query (key t BC + BC - 1 > wq0), and the number of the wave's tiles from there on
+  const int t_mask = CAUSAL ? min(Nk / BC, (wq0 - kofs + 1) / BC) : Nk / BC;
   const uint32_t n_masked = (uint32_t)max(w_kt - t_mask, 0);
 
   // ---- HBM -> LDS copies: lane l of a wave's copy i of a tile writes 16-byte chunk
@@ -235,7 +256,7 @@ fa_fwd_wide_kernel(const Params p) {
   auto tile_rsrc = [&](const uint16_t* src, int t) {
     const int k0 = min(t, n_kt - 1) * BC;
     return buffer_rsrc((uint64_t)(uintptr_t)(src + (size_t)k0 * D),
-                       t < n_kt ? (uint32_t)(min(N - k0, BC) * D * 2) : 0u);
+                       t < n_kt ? (uint32_t)(min(Nk - k0, BC) * D * 2) : 0u);
   };
   const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(kbuf + wid * 64));
   const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(vbuf + wid * 64));
@@ -264,7 +285,9 @@ fa_fwd_wide_kernel(const Params p) {
   // the last, read as zeros as above. (The address's high word is used as it is: device
   // addresses stay below 2^48, so it never reaches the resource's stride field.)
   constexpr uint32_t TB = (uint32_t)CHUNKS * 16u;  // bytes of a K (or V) tile
-  const uint32_t kv_bytes = (uint32_t)min(n_kt * BC, N) * (uint32_t)(D * 2);
+  // (an empty split has n_kt <= 0: no bytes)
+  const int kv_rows = SPLIT ? max(min(n_kt * BC, Nk), 0) : min(n_kt * BC, Nk);
+  const uint32_t kv_bytes = (uint32_t)kv_rows * (uint32_t)(D * 2);
   const uint16_t* kgj = kg;
   const uint16_t* vgj = vg;
   uint32_t remj = kv_bytes;
@@ -399,21 +422,21 @@ fa_fwd_wide_kernel(const Params p) {
 
   // S^T of tile t with its K rows read from global memory (the tile's ring slot may
   // already hold a later tile): same operands, same accumulation order as qk_plain, so
-  // the same bits. Rows past N read row N - 1; the mask clears them.
+  // the same bits. Rows past the last key read the last key; the mask clears them.
   auto qk_global = [&](int t, STile& s) {
     zero(s);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int kb = i % (BC / 32), ds = i / (BC / 32);
-      const int row = min(t * BC + kb * 32 + key_of_row(l32), N - 1);
+      const int row = min(t * BC + kb * 32 + key_of_row(l32), Nk - 1);
       const u32x4_t kf = ld16(kg + (size_t)row * D + ds * 16 + hh * 8);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) s[kb][qb] = E::mfma(kf, qf[qb][ds], s[kb][qb]);
     }
   };
 
-  // -inf on keys past N and, under the causal mask, on keys after the query; only tiles
-  // that reach past N or cross the diagonal need it
+  // -inf on keys past the last one and, under the causal mask, on keys after the query;
+  // only tiles that reach past the keys or cross the diagonal need it
   auto mask = [&](STile& s, int j) __attribute__((always_inline)) {
     // tiles [t_mask, w_kt) need it (tiles past the wave's last one are never used)
     if ((uint32_t)(j - t_mask) >= n_masked) return;
@@ -427,7 +450,7 @@ fa_fwd_wide_kernel(const Params p) {
         if (kb + qb > 0) asm volatile("" : "+v"(s[kb][qb]));
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int last = CAUSAL ? min(N - 1, qbase[qb] + l32) : N - 1;
+      const int last = CAUSAL ? min(Nk - 1, qbase[qb] + l32 - kofs) : Nk - 1;
       const int t = last - base;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
@@ -444,7 +467,7 @@ fa_fwd_wide_kernel(const Params p) {
   // computed in the slot that issues it.
   constexpr int LB = 1, LC = 2, NTQ = LB + 1, NPQ = LC - LB + 1;
   float tq[NTQ][2], pq[NPQ][2];
-#define FA_W_OPS kOpSched<NPAIR, NSLOT, LB, LC, SC_N, NQK, NPV, FA_W_PF, NDMA>
+#define FA_W_OPS kOpSched<NPAIR, NSLOT, LB, LC, SC_N, NQK, NPV, PF, NDMA>
   // op o of the stream: see make_op_sched
   auto exp_op = [&](const STile& s, PTile& pt, int o) __attribute__((always_inline)) {
     const int v = FA_W_OPS.code[o] / 8, op = FA_W_OPS.code[o] % 8;
@@ -545,7 +568,7 @@ fa_fwd_wide_kernel(const Params p) {
   // it consumes dies while the next one is produced, and the S^T tile it produces is
   // born after half the softmax tile has been consumed, which keeps the live registers
   // down. The softmax ops of tile j+1 are spread over all slots. LDS operand
-  // reads run FA_W_PF steps ahead: the first K operands of the S^T block are read in the
+  // reads run PF steps ahead: the first K operands of the S^T block are read in the
   // last P V slots, the first V^T operands of the next iteration in the last S^T slots
   // (from a slot no copy of the next iteration touches). This wave's copies of K_{j+R+1}
   // and V_{j+R-1} (into the slots of K_{j+1} and V_{j-1}, both read in the previous
@@ -556,7 +579,7 @@ fa_fwd_wide_kernel(const Params p) {
   // dropped (no branch inside the slots).
   constexpr int COPY_EVERY = 2;
   static_assert(COPY_EVERY * NDMA <= SC_N, "copies spread over the P V block");
-  u32x4_t vq[FA_W_PF];  // the first V^T operands of the next P V block
+  u32x4_t vq[PF];  // the first V^T operands of the next P V block
   auto iteration = [&](int u, int j, STile& s_new, const STile& s_mid, PTile& p_mid,
                        const PTile& p_cur) __attribute__((always_inline)) {
     // ring slots: tile t is in slot t % R, and j % R = u
@@ -564,7 +587,7 @@ fa_fwd_wide_kernel(const Params p) {
     u32x4_t vf[NPV];
     u32x4_t kf[NQK];
 #pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) vf[i] = vq[i];
+    for (int i = 0; i < PF; ++i) vf[i] = vq[i];
 #pragma unroll
     for (int sc = 0; sc < SC_N; ++sc) {
       const int i = sc / 2, qb = sc % 2, db = i % (D / 32), st = i / (D / 32);
@@ -574,16 +597,16 @@ fa_fwd_wide_kernel(const Params p) {
         asm volatile("" ::"v"(vf[i - 1]), "v"(p_cur[0][(i - 1) / (D / 32)]),
                      "v"(p_cur[1][(i - 1) / (D / 32)]));
       // one LDS wait per two steps: the operands of steps i and i + 1 together (read
-      // FA_W_PF and FA_W_PF - 1 steps before)
+      // PF and PF - 1 steps before)
       if (qb == 0 && i % 2 == 0 && i + 1 < NPV) asm volatile("" ::"v"(vf[i]), "v"(vf[i + 1]));
       mfma_acc_agpr<BF16>(oacc[db][qb], vf[i], p_cur[qb][st]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + FA_W_PF < NPV) {
-        const u32x2_t h = v_half(vst, i + FA_W_PF, qb);
-        vf[i + FA_W_PF][2 * qb] = h[0];
-        vf[i + FA_W_PF][2 * qb + 1] = h[1];
+      if (i + PF < NPV) {
+        const u32x2_t h = v_half(vst, i + PF, qb);
+        vf[i + PF][2 * qb] = h[0];
+        vf[i + PF][2 * qb + 1] = h[1];
       }
-      if (qb == 0 && i >= NPV - FA_W_PF) kf[i - (NPV - FA_W_PF)] = k_frag(kst, i - (NPV - FA_W_PF));
+      if (qb == 0 && i >= NPV - PF) kf[i - (NPV - PF)] = k_frag(kst, i - (NPV - PF));
       if (sc % COPY_EVERY == 1) copy_loop(u, sc / COPY_EVERY);
 #pragma unroll
       for (int o = FA_W_OPS.first[sc]; o < FA_W_OPS.first[sc + 1]; ++o) exp_op(s_mid, p_mid, o);
@@ -601,11 +624,11 @@ fa_fwd_wide_kernel(const Params p) {
       }
       s_new[kb][qb] = E::mfma(kf[i], qf[qb][ds], s_new[kb][qb]);
       __builtin_amdgcn_sched_barrier(0);
-      if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(kst, i + FA_W_PF);
-      if (i >= NQK - FA_W_PF) {
-        const u32x2_t h = v_half(vnext, i - (NQK - FA_W_PF), qb);
-        vq[i - (NQK - FA_W_PF)][2 * qb] = h[0];
-        vq[i - (NQK - FA_W_PF)][2 * qb + 1] = h[1];
+      if (qb == 0 && i + PF < NQK) kf[i + PF] = k_frag(kst, i + PF);
+      if (i >= NQK - PF) {
+        const u32x2_t h = v_half(vnext, i - (NQK - PF), qb);
+        vq[i - (NQK - PF)][2 * qb] = h[0];
+        vq[i - (NQK - PF)][2 * qb + 1] = h[1];
       }
 #pragma unroll
       for (int o = FA_W_OPS.first[sl]; o < FA_W_OPS.first[sl + 1]; ++o) exp_op(s_mid, p_mid, o);
@@ -617,12 +640,12 @@ fa_fwd_wide_kernel(const Params p) {
   // ---- ring waits and barriers --------------------------------------------------------
   // At the end of iteration j every copy but this iteration's must have landed (the next
   // iteration reads K_{j+3}, V_{j+1}, and at its end V_{j+2}), and the barrier must follow
-  // this wave's last K read (the 2 FA_W_PF V^T reads for the next iteration issued
+  // this wave's last K read (the 2 PF V^T reads for the next iteration issued
   // after it may stay in flight: no copy of the next iteration goes into their slot).
   auto end_wait = [&]() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory"); };
   auto ring_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   auto loop_barrier = [&]() {
-    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(2 * FA_W_PF) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(2 * PF) : "memory");
   };
 
   // ---- prologue: S^T and softmax of tile 0, S^T of tile 1 -----------------------------
@@ -656,13 +679,13 @@ fa_fwd_wide_kernel(const Params p) {
     zero(sb);
     u32x4_t kf[NQK];
 #pragma unroll
-    for (int i = 0; i < FA_W_PF; ++i) kf[i] = k_frag(1, i);
+    for (int i = 0; i < PF; ++i) kf[i] = k_frag(1, i);
 #pragma unroll
     for (int sl = 0; sl < SB_N; ++sl) {
       const int i = sl / 2, qb = sl % 2, kb = i % (BC / 32), ds = i / (BC / 32);
       sb[kb][qb] = E::mfma(kf[i], qf[qb][ds], sb[kb][qb]);
       __builtin_amdgcn_sched_barrier(0);
-      if (qb == 0 && i + FA_W_PF < NQK) kf[i + FA_W_PF] = k_frag(1, i + FA_W_PF);
+      if (qb == 0 && i + PF < NQK) kf[i + PF] = k_frag(1, i + PF);
 #pragma unroll
       for (int o = FA_W_OPS.n * sl / SB_N; o < FA_W_OPS.n * (sl + 1) / SB_N; ++o)
         exp_op(sa, pa, o);
@@ -683,7 +706,7 @@ fa_fwd_wide_kernel(const Params p) {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PW) : "memory");
   ring_barrier();
 #pragma unroll
-  for (int i = 0; i < FA_W_PF; ++i)
+  for (int i = 0; i < PF; ++i)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const u32x2_t x = v_half(0, i, h);
@@ -723,7 +746,38 @@ fa_fwd_wide_kernel(const Params p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
-  {
+  if constexpr (SPLIT) {
+    // the split's normalized partial O (float32) and partial L, straight from registers:
+    // lane (query qbase[qb] + l32, half hh) holds head dims 32 db + 8 g + 4 hh + 0..3
+    if (!wave_live) return;
+    const float kLn2 = 0.69314718055994530942f;
+    // (an opaque copy of the lane index keeps the row addresses below from being computed
+    // before the loop and held in registers across it)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      drain_o(qb);
+      const float l_tot = xhalf_sum(ls[qb][0] + ls[qb][1]);
+      const float inv = empty ? 0.f : 1.0f / l_tot;  // an empty split's O~ is 0
+      const int qi = qbase[qb] + (ln & 31);
+      if (qi < N) {
+        const size_t row = ((size_t)split * p.BH + bh) * N + qi;
+        float* prow = p.o_part + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16_t& a = oacc[db][qb];
+            *reinterpret_cast<float4*>(prow + db * 32 + g * 8 + (ln >> 5) * 4) =
+                float4{a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+          }
+        if (ln < 32)
+          p.l_part[row] = empty ? -__builtin_inff() : (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      }
+    }
+    return;
+  } else {
     static_assert(R * CHUNKS >= NW * 64 * CPR && (CPR & (CPR - 1)) == 0 && CPR <= 64,
                   "a 64-row O tile per wave fits the K ring");
     ring_barrier();
