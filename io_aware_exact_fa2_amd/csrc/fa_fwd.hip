@@ -22,22 +22,17 @@ using fa_host::cu_count;
 using fa_host::g_last_hip_error;
 using fa_host::ranges_overlap;
 
-// Launch shapes. The fast path (d = 64, 128) is tunable at build time for sweeps;
-// the defaults are the measured best. The generic path (other d) is fixed.
+// Launch shapes. The fast paths (the 32-query kernel at d = 64, the wide kernel at
+// d = 128) are tunable at build time for sweeps; the defaults are the measured best. The
+// generic path (other d) is fixed.
 #ifndef FA_FAST_NW
 #define FA_FAST_NW 4      // waves per workgroup (8: -3% on the d = 64 workloads)
-#endif
-#ifndef FA_BC_D128
-#define FA_BC_D128 64     // keys per tile at d = 128
 #endif
 #ifndef FA_BC_D64
 #define FA_BC_D64 64      // keys per tile at d = 64
 #endif
-#ifndef FA_WPE_D128
-#define FA_WPE_D128 2     // waves per SIMD the d = 128 kernel is register-limited to
-#endif
 #ifndef FA_WPE_D64
-#define FA_WPE_D64 2
+#define FA_WPE_D64 2      // least waves per SIMD the d = 64 kernel's registers must allow
 #endif
 #ifndef FA_WIDE_RING
 #define FA_WIDE_RING 4    // LDS ring slots per tensor
@@ -83,12 +78,11 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_fast(fa::Params p, hipStream_t stream) {
-  constexpr int WPE = D == 128 ? FA_WPE_D128 : FA_WPE_D64;
-  constexpr int BC = D == 128 ? FA_BC_D128 : FA_BC_D64;
+  static_assert(D == 64, "the 32-query kernel serves d = 64");
   constexpr int BR = kFNW * 32;
   p.n_qt = (p.N + BR - 1) / BR;
   const int grid = p.n_qt * p.BH;
-  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, BC, WPE>;
+  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, FA_BC_D64, FA_WPE_D64>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
   return hipGetLastError();
 }

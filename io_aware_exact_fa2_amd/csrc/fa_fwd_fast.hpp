@@ -1,5 +1,6 @@
-// fa_fwd_fast.hpp — FA2-order attention forward for gfx950 (MI355X), fast path for
-// head dims 64 and 128.
+// fa_fwd_fast.hpp — FA2-order attention forward for gfx950 (MI355X), 32 queries per wave:
+// the fast path for head dim 64 (the template also builds at 128, which the library
+// serves with the wide kernel).
 //
 // Algorithm ([P1] currybab.bearblog.dev, "Triton으로 FlashAttention 구현하기 전에 -
 // FA1, 2 forward pass", section "FlashAttention 2 forward pass 알고리즘 분석"): the
@@ -63,10 +64,7 @@
 #define FA_SG_C_VALU 2    // VALU per P V MFMA step (row max of the next tile)
 #endif
 #ifndef FA_SG_PREFETCH
-#define FA_SG_PREFETCH 2  // MFMA steps an LDS operand read runs ahead (d = 128)
-#endif
-#ifndef FA_SG_PREFETCH_D64
-#define FA_SG_PREFETCH_D64 5  // the same at d = 64 (2: 2.4% slower at B=8, H=32, N=4000)
+#define FA_SG_PREFETCH 5  // MFMA steps an LDS operand read runs ahead (2: 2.4% slower at d = 64)
 #endif
 #ifndef FA_SG_ON
 #define FA_SG_ON 1
@@ -100,7 +98,7 @@ fa_fwd_fast_kernel(const Params p) {
   constexpr int CPR = G::CPR, NQK = G::NQK, NPV = G::NPV;
   constexpr int SPS = (BC / 2) / NQK;  // scores exponentiated per S^T step
   constexpr int MPS = (BC / 2) / NPV;  // scores max-reduced per P V step
-  constexpr int SGP = D == 64 ? FA_SG_PREFETCH_D64 : FA_SG_PREFETCH;
+  constexpr int SGP = FA_SG_PREFETCH;
   static_assert(SPS % 2 == 0 && MPS >= 1, "pipeline step split");
   __shared__ u32x4_t ks0[G::CHUNKS];
   __shared__ u32x4_t vs0[G::CHUNKS];
