@@ -242,6 +242,13 @@ def test_workspace_pass_validation(L, no_gpu, which):
             <= 3 * per_split(300) + 512
         assert 8 * per_split(1000) <= fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 64, 8) \
             <= 8 * per_split(1000) + 512
+        # at d = 128 the tile is the wide kernel's 256 rows: N = 300 with 8 requested splits
+        # runs 2 (256 keys each), N = 1000 with 8 runs 4
+        per_split128 = lambda n: n * 128 * 4 + n * 4  # noqa: E731
+        assert 2 * per_split128(300) <= fa.fa_fwd_splitkv_workspace_size(1, 1, 300, 128, 8) \
+            <= 2 * per_split128(300) + 512
+        assert 4 * per_split128(1000) <= fa.fa_fwd_splitkv_workspace_size(1, 1, 1000, 128, 8) \
+            <= 4 * per_split128(1000) + 512
     assert fa.fa_last_hip_error() == 0
 
 
