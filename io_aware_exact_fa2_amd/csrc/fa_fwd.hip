@@ -34,6 +34,9 @@ using fa_host::ranges_overlap;
 #ifndef FA_WPE_D64
 #define FA_WPE_D64 2      // least waves per SIMD the d = 64 kernel's registers must allow
 #endif
+#ifndef FA_QB_D64
+#define FA_QB_D64 1       // 32-query blocks per wave at d = 64 (2: over 32-key tiles)
+#endif
 #ifndef FA_WIDE_RING
 #define FA_WIDE_RING 4    // LDS ring slots per tensor
 #endif
@@ -79,10 +82,12 @@ int validate(const void* q, const void* k, const void* v, const void* o, const f
 template <bool BF16, int D, bool CAUSAL>
 hipError_t launch_fast(fa::Params p, hipStream_t stream) {
   static_assert(D == 64, "the 32-query kernel serves d = 64");
-  constexpr int BR = kFNW * 32;
+  constexpr int QB = FA_QB_D64;
+  constexpr int BC = QB == 2 ? 32 : FA_BC_D64;
+  constexpr int BR = kFNW * 32 * QB;
   p.n_qt = (p.N + BR - 1) / BR;
   const int grid = p.n_qt * p.BH;
-  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, FA_BC_D64, FA_WPE_D64>;
+  auto kern = fa::fa_fwd_fast_kernel<BF16, D, CAUSAL, kFNW, BC, FA_WPE_D64, false, QB>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kFNW * 64), 0, stream, p);
   return hipGetLastError();
 }

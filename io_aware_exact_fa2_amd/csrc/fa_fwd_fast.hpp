@@ -72,12 +72,13 @@
 
 namespace fa {
 
-template <int D_, int NW_, int BC_>
+template <int D_, int NW_, int BC_, int QB_ = 1>
 struct FastGeom {
   static constexpr int D = D_;
   static constexpr int NW = NW_;
   static constexpr int BC = BC_;
-  static constexpr int BR = NW * 32;             // queries per workgroup (32 per wave)
+  static constexpr int QB = QB_;                 // 32-query blocks per wave
+  static constexpr int BR = NW * 32 * QB;        // queries per workgroup
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int CHUNKS = BC * CPR;        // chunks per K (or V) tile
   static constexpr int INSTR = CHUNKS / 64;      // 1 KB wave copies per tile and tensor
@@ -88,16 +89,18 @@ struct FastGeom {
   static_assert(BC % 32 == 0 && CHUNKS % 64 == 0, "whole MFMA blocks and wave copies");
   static_assert(INSTR % NW == 0 && PER_WAVE >= 1, "every wave issues the same copies");
   static_assert(2 * PER_WAVE <= NQK, "copies fit in the S^T pipeline steps");
+  static_assert(QB == 1 || QB == 2, "one or two query blocks per wave");
 };
 
-template <bool BF16, int D, bool CAUSAL, int NW, int BC, int WPE, bool SPLIT = false>
+template <bool BF16, int D, bool CAUSAL, int NW, int BC, int WPE, bool SPLIT = false, int QB = 1>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fa_fwd_fast_kernel(const Params p) {
-  using G = FastGeom<D, NW, BC>;
+  using G = FastGeom<D, NW, BC, QB>;
   using E = Elt<BF16>;
   constexpr int CPR = G::CPR, NQK = G::NQK, NPV = G::NPV;
-  constexpr int SPS = (BC / 2) / NQK;  // scores exponentiated per S^T step
-  constexpr int MPS = (BC / 2) / NPV;  // scores max-reduced per P V step
+  constexpr int NSC = QB * (BC / 2);   // scores per lane and tile
+  constexpr int SPS = NSC / NQK;       // scores exponentiated per S^T step
+  constexpr int MPS = NSC / NPV;       // scores max-reduced per P V step
   constexpr int SGP = FA_SG_PREFETCH;
   static_assert(SPS % 2 == 0 && MPS >= 1, "pipeline step split");
   __shared__ u32x4_t ks0[G::CHUNKS];
@@ -130,12 +133,19 @@ fa_fwd_fast_kernel(const Params p) {
   const uint16_t* __restrict__ kg = p.k + head + (size_t)kofs * D;
   const uint16_t* __restrict__ vg = p.v + head + (size_t)kofs * D;
 
+  static_assert(!(SPLIT && QB == 2), "the split-KV pass runs one query block per wave");
   const int q0 = qt * G::BR;
-  const int wq0 = q0 + wid * 32;
+  // wave w owns the 32-query block w, and with two blocks per wave also block
+  // 2 NW - 1 - w (under the causal mask the two blocks' work then differs by the same
+  // amount in every wave)
+  int qbase[QB];
+  qbase[0] = q0 + wid * 32;
+  if constexpr (QB == 2) qbase[QB - 1] = q0 + 32 * (2 * NW - 1 - wid);
+  const int wq0 = qbase[0];  // the wave's first query
   const int q_end = min(q0 + G::BR, N);
   const int n_kt = CAUSAL ? (min(q_end - kofs, Nk) + BC - 1) / BC : (Nk + BC - 1) / BC;
   const bool wave_live = wq0 < N;
-  const int w_last_q = min(wq0 + 32, N) - 1;
+  const int w_last_q = min(qbase[QB - 1] + 32, N) - 1;
   const int w_kt = CAUSAL ? min(n_kt, (w_last_q - kofs) / BC + 1) : n_kt;
   if constexpr (SPLIT) {
     // Splits start at multiples of the query tile, so under the causal mask a split
@@ -195,24 +205,30 @@ fa_fwd_fast_kernel(const Params p) {
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T), in registers for the whole loop ------
-  u32x4_t qf[D / 16];
-  {
-    const int qi = wq0 + l32;
+  u32x4_t qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qbase[qb] + l32;
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
       u32x4_t x = {0u, 0u, 0u, 0u};
       if (qi < N) x = ld16(qg + (size_t)qi * D + ds * 16 + hh * 8);
-      qf[ds] = x ^ p.qsign;
+      qf[qb][ds] = x ^ p.qsign;
     }
   }
 
   // ---- running state ---------------------------------------------------------------
-  f32x16_t oacc[D / 32];
+  f32x16_t oacc[QB][D / 32];
+  float ms[QB], l_part[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float ms = 0.f, l_part = 0.f;
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
+    ms[qb] = 0.f;
+    l_part[qb] = 0.f;
+  }
   const float c = p.c;
 
   // ---- per-lane LDS read addresses ---------------------------------------------------
@@ -258,13 +274,16 @@ fa_fwd_fast_kernel(const Params p) {
     return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
   };
 
-  typedef f32x16_t STile[BC / 32];  // S^T accumulators of one key tile
-  // score e of a tile: key block e / 16, accumulator register e % 16
+  typedef f32x16_t STile[BC / 32][QB];  // S^T accumulators of one key tile
+  // score e of a tile: query block e / (BC / 2); within it, f = e % (BC / 2) is key
+  // block f / 16, accumulator register f % 16
   auto zero = [](STile& s) {
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
   };
 
   // -inf on keys past N and, under the causal mask, on keys after the query; only
@@ -273,108 +292,138 @@ fa_fwd_fast_kernel(const Params p) {
     const int k0 = j * BC;
     const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wq0 - kofs);
     if (!masked) return;
-    const int qi = wq0 + l32 - kofs;  // the query, in key coordinates
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = qbase[qb] + l32 - kofs;  // the query, in key coordinates
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kb * 32 + key_of_reg(r, hh);
-        if (key >= Nk || (CAUSAL && key > qi)) s[kb][r] = -__builtin_inff();
-      }
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + key_of_reg(r, hh);
+          if (key >= Nk || (CAUSAL && key > qi)) s[kb][qb][r] = -__builtin_inff();
+        }
+    }
   };
 
   // m_new = max(m_old, rowmax S); alpha = exp2(m_old - m_new) rescales l and O~. The
   // whole wave skips it when no row needs it (alpha = 1), or, with tau > 0, when no
   // row's max rose by more than tau (log2 units).
-  auto grow_max = [&](float mxs) {
-    if (__builtin_amdgcn_ballot_w64(mxs > ms + p.tau) != 0) {
-      const float ms_new = __builtin_fmaxf(ms, mxs);
-      const float alpha = __builtin_amdgcn_exp2f(ms - ms_new);
-      ms = ms_new;
-      l_part *= alpha;
+  auto grow_max = [&](int qb, float mxs) {
+    if (__builtin_amdgcn_ballot_w64(mxs > ms[qb] + p.tau) != 0) {
+      const float ms_new = __builtin_fmaxf(ms[qb], mxs);
+      const float alpha = __builtin_amdgcn_exp2f(ms[qb] - ms_new);
+      ms[qb] = ms_new;
+      l_part[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
     }
   };
 
-  u32x4_t pb[BC / 16];  // P~ of the current tile, packed as P V operands
+  u32x4_t pb[QB][BC / 16];  // P~ of the current tile, packed as P V operands
 
   // Block B: S^T of tile j+1 (MFMA) interleaved with the exponentials of tile j (VALU)
-  // and this wave's copies of the following tiles (VMEM).
+  // and this wave's copies of the following tiles (VMEM). Each K operand read from LDS
+  // feeds one MFMA per query block.
   auto qk_exp = [&](const u32x4_t* k_next, STile& s_next, const STile& s_cur,
                     const Copies& cp) {
     zero(s_next);
-    const float msc = ms;
-    float lsum0 = 0.f, lsum1 = 0.f;
+    float msc[QB], lsum[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      msc[qb] = ms[qb];
+      lsum[qb][0] = 0.f;
+      lsum[qb][1] = 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int kb = i % (BC / 32), ds = i / (BC / 32);
-      s_next[kb] = E::mfma(k_frag(k_next, i), qf[ds], s_next[kb]);
+      const u32x4_t kf = k_frag(k_next, i);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s_next[kb][qb] = E::mfma(kf, qf[qb][ds], s_next[kb][qb]);
 #pragma unroll
       for (int e = i * SPS; e < (i + 1) * SPS; e += 2) {
+        const int qb = e / (BC / 2), f = e % (BC / 2);
         // c > 0 on this path, so a masked score (-inf) gives exp2(-inf) = 0 exactly
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e / 16][e % 16], c, -msc));
+        const float p0 =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[f / 16][qb][f % 16], c, -msc[qb]));
         const float p1 =
-            __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e / 16][(e + 1) % 16], c, -msc));
+            __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[f / 16][qb][(f + 1) % 16], c, -msc[qb]));
         const uint32_t w = E::pack(p0, p1);
-        pb[e / 8][(e % 8) / 2] = w;
+        pb[qb][f / 8][(f % 8) / 2] = w;
         if constexpr (BF16) {
-          lsum0 += p0;
-          lsum1 += p1;
+          lsum[qb][0] += p0;
+          lsum[qb][1] += p1;
         } else {
           // half-precision P: l sums the rounded pair (one dot2), each term within 2^-11
           // of its probability, so L moves by at most that relative amount
-          float& acc = (e / 2) % 2 ? lsum1 : lsum0;
+          float& acc = lsum[qb][(f / 2) % 2];
           acc = E::sum2(w, acc);
         }
       }
       copy_step(cp, i);
     }
-    l_part += lsum0 + lsum1;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_part[qb] += lsum[qb][0] + lsum[qb][1];
     // keep the exponentials in this block (no sinking into the P V block): a use of the
     // packed operands here. (A tied in/out operand did the same but cost 8 register
     // moves per tile to bring them back into the operand registers.)
 #pragma unroll
-    for (int st = 0; st < BC / 16; ++st) asm volatile("" ::"v"(pb[st]));
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int st = 0; st < BC / 16; ++st) asm volatile("" ::"v"(pb[qb][st]));
 #if FA_SG_ON
     __builtin_amdgcn_sched_group_barrier(0x100, SGP, 0);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, FA_SG_B_VALU, 0);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_SG_B_VALU, 0);
+      }
       if (i < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (i + SGP < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #endif
   };
 
-  // Block C: P V of tile j (MFMA) interleaved with the row max of tile j+1 (VALU)
-  auto pv_max = [&](const u32x4_t* v_cur, const STile& s_next) {
-    float m0 = -__builtin_inff(), m1 = -__builtin_inff();
+  // Block C: P V of tile j (MFMA) interleaved with the row max of tile j+1 (VALU); each
+  // V^T operand read feeds one MFMA per query block. mx: the lane's max per query block.
+  auto pv_max = [&](const u32x4_t* v_cur, const STile& s_next, float (&mx)[QB]) {
+    float m[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m[qb][0] = m[qb][1] = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       const int db = i % (D / 32), st = i / (D / 32);
-      oacc[db] = E::mfma(v_frag(v_cur, i), pb[st], oacc[db]);
+      const u32x4_t vf = v_frag(v_cur, i);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(vf, pb[qb][st], oacc[qb][db]);
 #pragma unroll
       for (int e = i * MPS; e < (i + 1) * MPS; ++e) {
-        if (e & 1) m1 = __builtin_fmaxf(m1, s_next[e / 16][e % 16]);
-        else m0 = __builtin_fmaxf(m0, s_next[e / 16][e % 16]);
+        const int qb = e / (BC / 2), f = e % (BC / 2);
+        m[qb][e & 1] = __builtin_fmaxf(m[qb][e & 1], s_next[f / 16][qb][f % 16]);
       }
     }
-    float mx = __builtin_fmaxf(m0, m1);
-    asm volatile("" : "+v"(mx));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float x = __builtin_fmaxf(m[qb][0], m[qb][1]);
+      asm volatile("" : "+v"(x));
+      mx[qb] = x;
+    }
 #if FA_SG_ON
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * SGP, 1);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, FA_SG_C_VALU, 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_SG_C_VALU, 1);
+      }
       if (i + SGP < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
     }
 #endif
-    return mx;
   };
 
   // One key tile j whose masked S^T is in s_cur and whose max is already folded into
@@ -385,8 +434,12 @@ fa_fwd_fast_kernel(const Params p) {
                   const u32x4_t* v_cur, int j, bool next, const Copies& cp) {
     qk_exp(k_next, s_next, s_cur, cp);
     mask(s_next, j + 1);
-    const float mx = pv_max(v_cur, s_next);
-    if (next) grow_max(xhalf_max(mx) * c);
+    float mx[QB];
+    pv_max(v_cur, s_next, mx);
+    if (next) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) grow_max(qb, xhalf_max(mx[qb]) * c);
+    }
   };
 
   // ---- main loop ---------------------------------------------------------------------
@@ -407,15 +460,20 @@ fa_fwd_fast_kernel(const Params p) {
 #pragma unroll
     for (int i = 0; i < NQK; ++i) {
       const int kb = i % (BC / 32), ds = i / (BC / 32);
-      sa[kb] = E::mfma(k_frag(ks0, i), qf[ds], sa[kb]);
+      const u32x4_t kf = k_frag(ks0, i);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = E::mfma(kf, qf[qb][ds], sa[kb][qb]);
     }
     mask(sa, 0);
-    float mx = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -__builtin_inff();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sa[kb][r]);
-    ms = xhalf_max(mx) * c;  // tile 0 holds key 0, allowed for every row: finite
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sa[kb][qb][r]);
+      ms[qb] = xhalf_max(mx) * c;  // tile 0 holds key 0, allowed for every row: finite
+    }
   }
   __syncthreads();  // every wave is done with ks0 before K_2 overwrites it
   for (int j = 0; j < n_kt; j += 2) {
@@ -435,47 +493,84 @@ fa_fwd_fast_kernel(const Params p) {
   // ---- epilogue: O = O~ / l, L = (m*c + log2 l) * ln 2 ------------------------------
   if (!wave_live) return;
   const float kLn2 = 0.69314718055994530942f;
-  const float l_tot = xhalf_sum(l_part);
-  const int qi = wq0 + l32;  // rows past N (finite, from clamped or zero rows) are never stored
-  const float inv = 1.0f / l_tot;
-  if constexpr (SPLIT) {
-    if (qi >= N) return;
-    const size_t row = ((size_t)split * p.BH + bh) * N + qi;
-    float* prow = p.o_part + row * D;
+  if constexpr (QB == 1) {
+    const float l_tot = xhalf_sum(l_part[0]);
+    const int qi = wq0 + l32;  // rows past N (finite, from clamped or zero rows) are never stored
+    const float inv = 1.0f / l_tot;
+    if constexpr (SPLIT) {
+      if (qi >= N) return;
+      const size_t row = ((size_t)split * p.BH + bh) * N + qi;
+      float* prow = p.o_part + row * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& a = oacc[0][db];
+          *reinterpret_cast<float4*>(prow + db * 32 + g * 8 + hh * 4) =
+              float4{a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+        }
+      if (hh == 0) p.l_part[row] = (ms[0] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      return;
+    }
+    // O leaves through LDS (the loop ended at a barrier after every copy landed, so the K
+    // and V slots are idle): the wave writes its 32 rows into its own part of them (a lane
+    // holds 8 bytes of one row per write) and stores 16-byte chunks of whole rows, instead
+    // of 8-byte pieces over 32 rows per store instruction, in the o_pos / o_swap layout.
+    static_assert(NW <= 4 && 2 * 32 * CPR <= G::CHUNKS, "two waves' O tiles fit one slot");
+    unsigned char* ot =
+        reinterpret_cast<unsigned char*>((wid < 2 ? ks0 : vs0) + (wid & 1) * 32 * CPR);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x16_t& a = oacc[db];
-        *reinterpret_cast<float4*>(prow + db * 32 + g * 8 + hh * 4) =
-            float4{a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+        const f32x16_t& a = oacc[0][db];
+        const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
+        const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+        const int c = db * 4 + g;  // 16-byte chunk of row l32; this lane holds half hh
+        *reinterpret_cast<u32x2_t*>(ot + o_half_off<CPR>(l32, c, hh)) = u32x2_t{w0, w1};
       }
-    if (hh == 0) p.l_part[row] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
-    return;
-  }
-  // O leaves through LDS (the loop ended at a barrier after every copy landed, so the K
-  // and V slots are idle): the wave writes its 32 rows into its own part of them (a lane
-  // holds 8 bytes of one row per write) and stores 16-byte chunks of whole rows, instead
-  // of 8-byte pieces over 32 rows per store instruction, in the o_pos / o_swap layout.
-  static_assert(NW <= 4 && 2 * 32 * CPR <= G::CHUNKS, "two waves' O tiles fit one slot");
-  unsigned char* ot = reinterpret_cast<unsigned char*>((wid < 2 ? ks0 : vs0) + (wid & 1) * 32 * CPR);
+    if (hh == 0 && qi < N)
+      p.lse[(size_t)bh * N + qi] = (ms[0] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x16_t& a = oacc[db];
-      const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
-      const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
-      const int c = db * 4 + g;  // 16-byte chunk of row l32; this lane holds half hh
-      *reinterpret_cast<u32x2_t*>(ot + o_half_off<CPR>(l32, c, hh)) = u32x2_t{w0, w1};
+    for (int it = 0; it < CPR / 2; ++it) {
+      const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
+      const u32x4_t x = o_chunk_read<CPR>(ot, rr, c);
+      if (wq0 + rr < N)
+        *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)(wq0 + rr) * D + c * 8) = x;
     }
-  if (hh == 0 && qi < N) p.lse[(size_t)bh * N + qi] = (ms + __builtin_amdgcn_logf(l_tot)) * kLn2;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+  } else {
+    // Two query blocks: the wave's 64 rows go through a staging area of their own (the
+    // key/value slots are too small for them), 16-byte chunks of whole rows per store,
+    // in the o_pos / o_swap layout; row 32 qb + r of the area is query qbase[qb] + r.
+    __shared__ __attribute__((aligned(16))) u32x4_t ostage[NW * 64 * CPR];
+    unsigned char* ot = reinterpret_cast<unsigned char*>(ostage + wid * 64 * CPR);
 #pragma unroll
-  for (int it = 0; it < CPR / 2; ++it) {
-    const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
-    const u32x4_t x = o_chunk_read<CPR>(ot, rr, c);
-    if (wq0 + rr < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)(wq0 + rr) * D + c * 8) = x;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = xhalf_sum(l_part[qb]);
+      const float inv = 1.0f / l_tot;
+      const int rr = 32 * qb + l32;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& a = oacc[qb][db];
+          const uint32_t w0 = E::pack(a[4 * g + 0] * inv, a[4 * g + 1] * inv);
+          const uint32_t w1 = E::pack(a[4 * g + 2] * inv, a[4 * g + 3] * inv);
+          *reinterpret_cast<u32x2_t*>(ot + o_half_off<CPR>(rr, db * 4 + g, hh)) = u32x2_t{w0, w1};
+        }
+      const int qi = qbase[qb] + l32;
+      if (hh == 0 && qi < N)
+        p.lse[(size_t)bh * N + qi] = (ms[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, in order
+#pragma unroll
+    for (int it = 0; it < CPR; ++it) {
+      const int rr = (64 / CPR) * it + lane / CPR, c = lane % CPR;
+      const u32x4_t x = o_chunk_read<CPR>(ot, rr, c);
+      const int qi = qbase[rr >> 5] + (rr & 31);
+      if (qi < N) *reinterpret_cast<u32x4_t*>(p.o + head + (size_t)qi * D + c * 8) = x;
+    }
   }
 }
 
