@@ -13,6 +13,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -283,11 +284,17 @@ def _is_kernel(name, path):
 
 
 def _is_split(name):
-    """The two kernels of the split-KV pass: the forward's split instantiation (its last
-    template argument) and the merge."""
-    return "fa_split_merge" in name or (
-        ("fa_fwd_fast_kernel" in name or "fa_fwd_wide_kernel" in name)
-        and name.split(">(")[0].endswith("true"))
+    """The kernels of the split-KV pass: a forward kernel's split instantiation (its
+    SPLIT template argument: the 7th of the 32-query kernel, the 6th of the wide kernel)
+    and the merge."""
+    if "fa_split_merge" in name:
+        return True
+    m = re.search(r"fa_fwd_(fast|wide)_kernel<([^>]*)>", name)
+    if m is None:
+        return False
+    args = [a.strip() for a in m.group(2).split(",")]
+    pos = 6 if m.group(1) == "fast" else 5
+    return len(args) > pos and args[pos] == "true"
 
 
 def _kernel_stats(directory, path):

@@ -128,7 +128,7 @@ def test_trace_summary_splitkv(tmp_path):
     against the plain forward's one kernel on the same shape."""
     w = workloads.get("few16k")
     fwd = "void fa::fa_fwd_wide_kernel<true, 128, false, 64, 4>(fa::Params)"
-    part = "void fa::fa_fwd_fast_kernel<true, 128, false, 4, 64, 2, true>(fa::Params)"
+    part = "void fa::fa_fwd_wide_kernel<true, 128, false, 64, 4, true>(fa::Params)"
     merge = "void fa::fa_split_merge_kernel<true, 128>(float const*, float const*, " \
             "unsigned short*, float*, long long, int)"
     kt = str(tmp_path / "kt")
@@ -150,3 +150,16 @@ def test_trace_summary_splitkv(tmp_path):
     assert r["splits"] == bench.SPLITKV["few16k"]
     md = (out / "fa_splitkv_rocprof.md").read_text()
     assert "| few16k | 4 | 400.0 |" in md and "(merge)" in md
+
+
+def test_split_kernel_names():
+    """The split-KV pass's kernels (either forward kernel's split instantiation, and the
+    merge) are told apart from the plain forward by name."""
+    assert bench._is_split("void fa::fa_fwd_wide_kernel<true, 128, true, 64, 4, true>(fa::Params)")
+    assert bench._is_split("void fa::fa_fwd_fast_kernel<false, 64, false, 4, 64, 2, true, 1>"
+                           "(fa::Params)")
+    assert not bench._is_split("void fa::fa_fwd_fast_kernel<false, 64, true, 4, 64, 2, false, 1>"
+                               "(fa::Params)")
+    assert bench._is_split("void fa::fa_split_merge_kernel<true, 128>(float const*)")
+    assert not bench._is_split("void fa::fa_fwd_wide_kernel<true, 128, false, 64, 4, false>"
+                               "(fa::Params)")
